@@ -1,0 +1,279 @@
+/*
+ * Plain fp64 CPU oracle for the selective state-space scan forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * benchmark's cpu_baseline leg may load this library.  The product path (the
+ * HIP library) shares no code with it.
+ *
+ * What it computes follows the pages' statement of the method, written out as
+ * the plain serial definition (no blocking, no reordering):
+ *
+ *  - Recurrence and readout (pwwt.cn article, section 1.1 "the recursion"):
+ *        h_t = Abar_t * h_{t-1} + Bbar_t * x_t,   y_t = C_t . h_t + D * x_t
+ *    with y_t using the state after step t has been absorbed and the same-step
+ *    C_t.
+ *  - Diagonal state transition per (channel, state), A = -exp(A_log) < 0 and
+ *    Delta = softplus(raw) > 0, so Abar = exp(Delta * A) lies in (0, 1)
+ *    (pwwt.cn section 2.4 "numerical stability").  Bbar * x is Delta * B * x.
+ *  - Optional clip of Delta after softplus (pwwt.cn section 3.3 "fusion
+ *    boundary": softplus, then upper/lower clip).
+ *  - Padding folded in as the identity element (a, b) = (1, 0) so that padded
+ *    steps leave the state unchanged (pwwt.cn section 2.3 "segments and
+ *    resets"); y at padded steps is +0.0 and the final state is the state after
+ *    the last valid step.
+ *  - Zero initial state unless h0 is given (pwwt.cn section 4.1, the naive
+ *    reference loop starts from zeros when no h0 is passed).
+ *
+ * Every input arrives as fp64 (bf16 and fp32 inputs convert exactly); all
+ * arithmetic is fp64 with the C library's exp/log1p.
+ *
+ * Readings taken where the pages are silent (see the design notes): Delta is
+ * passed raw and softplus is a step of the method; clamp after softplus;
+ * valid lengths are clamped to [0, L]; B and C are shared by all channels of a
+ * batch row.
+ *
+ * ORACLE_MUTATION (compile-time, tests only) plants one known mistake so the
+ * tests can show that their pins notice it.  0 = the correct oracle.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifndef ORACLE_MUTATION
+#define ORACLE_MUTATION 0
+#endif
+
+#if defined(__GNUC__)
+#define ORACLE_API __attribute__((visibility("default")))
+#else
+#define ORACLE_API
+#endif
+
+/* h_t = a_t * h_{t-1} + b_t for t = 0..L-1 starting from h0 (pwwt.cn section
+ * 2.1: the step as the affine map h -> a*h + b; section 4.1: the serial loop).
+ */
+ORACLE_API void oracle_scan_ab(const double* a, const double* b, double h0, int64_t L, double* h) {
+  double s = h0;
+  for (int64_t t = 0; t < L; ++t) {
+#if ORACLE_MUTATION == 1
+    s = a[t] * (s + b[t]); /* planted: input absorbed before the decay */
+#else
+    s = a[t] * s + b[t];
+#endif
+    h[t] = s;
+  }
+}
+
+/* softplus(v) = log(1 + e^v), written in the overflow-free form
+ * max(v, 0) + log1p(exp(-|v|)). */
+ORACLE_API double oracle_softplus(double v) {
+  double m = v > 0.0 ? v : 0.0;
+  return m + log1p(exp(-fabs(v)));
+}
+
+typedef struct {
+  const double *x, *delta, *A_log, *B, *C, *D, *h0;
+  const int32_t* valid_len;
+  int64_t nb, L, nd, N;
+  int softplus, clamp;
+  double dmin, dmax;
+} problem_t;
+
+/* One (b, d) row over all L steps.  y_out[t] for t in [0, L) with stride
+ * y_stride; h_out[n] for n in [0, N). */
+static void scan_row(const problem_t* p, int64_t b, int64_t d, double* y_out, int64_t y_stride, double* h_out,
+                     double* h /* scratch, N */, double* A /* scratch, N */) {
+  const int64_t L = p->L, N = p->N, nd = p->nd;
+  int64_t len = L;
+  if (p->valid_len) {
+    int64_t v = p->valid_len[b];
+    len = v < 0 ? 0 : (v > L ? L : v);
+  }
+  for (int64_t n = 0; n < N; ++n) {
+#if ORACLE_MUTATION == 3
+    A[n] = exp(p->A_log[d * N + n]); /* planted: sign of A dropped */
+#else
+    A[n] = -exp(p->A_log[d * N + n]);
+#endif
+    h[n] = p->h0 ? p->h0[(b * nd + d) * N + n] : 0.0;
+  }
+  const double dskip = p->D ? p->D[d] : 0.0;
+  for (int64_t t = 0; t < L; ++t) {
+    if (t >= len) {
+#if ORACLE_MUTATION == 7
+      for (int64_t n = 0; n < N; ++n) h[n] = 0.0; /* planted: padding resets the state */
+#endif
+      y_out[t * y_stride] = 0.0;
+      continue;
+    }
+    const int64_t i = (b * L + t) * nd + d;
+    const double xt = p->x[i];
+    double dt = p->delta[i];
+#if ORACLE_MUTATION != 5
+    if (p->softplus) dt = oracle_softplus(dt);
+#endif
+    if (p->clamp) {
+      if (dt < p->dmin) dt = p->dmin;
+      if (dt > p->dmax) dt = p->dmax;
+    }
+    const double* Bt = p->B + (b * L + t) * N;
+    const double* Ct = p->C + (b * L + t) * N;
+    double acc = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+      const double abar = exp(dt * A[n]);
+#if ORACLE_MUTATION == 6
+      const double bx = Bt[n] * xt; /* planted: Delta missing from the input term */
+#elif ORACLE_MUTATION == 8
+      const double bx = dt * Ct[n] * xt; /* planted: B and C swapped */
+#else
+      const double bx = dt * Bt[n] * xt;
+#endif
+#if ORACLE_MUTATION == 2
+      acc += Ct[n] * h[n]; /* planted: readout before the update */
+      h[n] = abar * h[n] + bx;
+#elif ORACLE_MUTATION == 1
+      h[n] = abar * (h[n] + bx);
+      acc += Ct[n] * h[n];
+#else
+      h[n] = abar * h[n] + bx;
+      acc += Ct[n] * h[n];
+#endif
+    }
+#if ORACLE_MUTATION == 4
+    y_out[t * y_stride] = acc; /* planted: skip term dropped */
+#else
+    y_out[t * y_stride] = acc + dskip * xt;
+#endif
+  }
+  if (h_out)
+    for (int64_t n = 0; n < N; ++n) h_out[n] = h[n];
+}
+
+typedef struct {
+  const problem_t* p;
+  const int64_t* rb;  /* NULL: all rows in (b, d) order */
+  const int64_t* rd;
+  int64_t nrows;
+  double* y;          /* full [B,L,D] when rb == NULL, else [nrows, L] */
+  double* h_last;     /* full [B,D,N] when rb == NULL, else [nrows, N]; may be NULL */
+  int64_t next;       /* static partition: worker k takes rows k, k+nthreads, ... */
+  int nthreads;
+  int status;
+} job_t;
+
+typedef struct {
+  job_t* job;
+  int k;
+} worker_arg_t;
+
+static void* worker(void* argp) {
+  worker_arg_t* wa = (worker_arg_t*)argp;
+  job_t* j = wa->job;
+  const problem_t* p = j->p;
+  double* scratch = (double*)malloc(sizeof(double) * 2 * (size_t)(p->N > 0 ? p->N : 1));
+  if (!scratch) {
+    j->status = -1;
+    return NULL;
+  }
+  for (int64_t r = wa->k; r < j->nrows; r += j->nthreads) {
+    int64_t b, d;
+    double *yo, *ho;
+    int64_t ystride;
+    if (j->rb) {
+      b = j->rb[r];
+      d = j->rd[r];
+      yo = j->y + r * p->L;
+      ystride = 1;
+      ho = j->h_last ? j->h_last + r * p->N : NULL;
+    } else {
+      b = r / p->nd;
+      d = r % p->nd;
+      yo = j->y + b * p->L * p->nd + d;
+      ystride = p->nd;
+      ho = j->h_last ? j->h_last + (b * p->nd + d) * p->N : NULL;
+    }
+    scan_row(p, b, d, yo, ystride, ho, scratch, scratch + p->N);
+  }
+  free(scratch);
+  return NULL;
+}
+
+static int run_job(job_t* job, int nthreads) {
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  if ((int64_t)nthreads > job->nrows) nthreads = job->nrows > 0 ? (int)job->nrows : 1;
+  job->nthreads = nthreads;
+  job->status = 0;
+  pthread_t tid[256];
+  worker_arg_t args[256];
+  int started = 0;
+  for (int k = 0; k < nthreads; ++k) {
+    args[k].job = job;
+    args[k].k = k;
+    if (k == 0) continue; /* worker 0 runs on the calling thread */
+    if (pthread_create(&tid[k], NULL, worker, &args[k]) != 0) {
+      job->status = -2;
+      break;
+    }
+    started = k;
+  }
+  worker(&args[0]);
+  for (int k = 1; k <= started; ++k) pthread_join(tid[k], NULL);
+  /* rows of workers that failed to start are done serially here */
+  if (job->status == -2) {
+    job->status = 0;
+    for (int k = started + 1; k < nthreads; ++k) worker(&args[k]);
+  }
+  return job->status;
+}
+
+/* Full forward over every (b, d) row.  Layouts (row-major, contiguous):
+ * x, delta, y: [nb, L, nd]; A_log: [nd, N]; B, C: [nb, L, N]; D: [nd] or NULL;
+ * valid_len: [nb] or NULL (all L); h0: [nb, nd, N] or NULL (zeros);
+ * h_last: [nb, nd, N] or NULL.  Returns 0, or a negative value on bad
+ * arguments or failed allocation. */
+ORACLE_API int oracle_selective_scan(const double* x, const double* delta, const double* A_log, const double* B,
+                                     const double* C, const double* D, const int32_t* valid_len, const double* h0,
+                                     int64_t nb, int64_t L, int64_t nd, int64_t N, int softplus, int clamp,
+                                     double dmin, double dmax, double* y, double* h_last, int nthreads) {
+  if (nb < 0 || L < 0 || nd < 0 || N < 1 || !y) return -3;
+  if (L > 0 && (!x || !delta || !B || !C)) return -3;
+  if (!A_log) return -3;
+  problem_t p = {x, delta, A_log, B, C, D, h0, valid_len, nb, L, nd, N, softplus, clamp, dmin, dmax};
+  job_t job;
+  memset(&job, 0, sizeof(job));
+  job.p = &p;
+  job.nrows = nb * nd;
+  job.y = y;
+  job.h_last = h_last;
+  return run_job(&job, nthreads);
+}
+
+/* The same forward restricted to the listed (row_b[r], row_d[r]) rows:
+ * y_rows [nrows, L] and h_rows [nrows, N] (h_rows may be NULL). */
+ORACLE_API int oracle_selective_scan_rows(const double* x, const double* delta, const double* A_log, const double* B,
+                                          const double* C, const double* D, const int32_t* valid_len,
+                                          const double* h0, int64_t nb, int64_t L, int64_t nd, int64_t N,
+                                          int softplus, int clamp, double dmin, double dmax, const int64_t* row_b,
+                                          const int64_t* row_d, int64_t nrows, double* y_rows, double* h_rows,
+                                          int nthreads) {
+  if (nb < 0 || L < 0 || nd < 0 || N < 1 || !y_rows || nrows < 0 || !row_b || !row_d) return -3;
+  if (L > 0 && (!x || !delta || !B || !C)) return -3;
+  if (!A_log) return -3;
+  for (int64_t r = 0; r < nrows; ++r)
+    if (row_b[r] < 0 || row_b[r] >= nb || row_d[r] < 0 || row_d[r] >= nd) return -3;
+  problem_t p = {x, delta, A_log, B, C, D, h0, valid_len, nb, L, nd, N, softplus, clamp, dmin, dmax};
+  job_t job;
+  memset(&job, 0, sizeof(job));
+  job.p = &p;
+  job.rb = row_b;
+  job.rd = row_d;
+  job.nrows = nrows;
+  job.y = y_rows;
+  job.h_last = h_rows;
+  return run_job(&job, nthreads);
+}
+
+ORACLE_API int oracle_mutation_id(void) { return ORACLE_MUTATION; }

@@ -1,0 +1,331 @@
+"""Pins of the CPU oracle to facts fixed by the pages and by mathematics.
+
+Each ``pin_*`` function takes the oracle module and a mutation id (0 = the real
+oracle; >0 = a build with one planted mistake) and raises AssertionError when
+the oracle disagrees with the pinned fact.  None of them re-types the oracle's
+loop: the expectations come from a printed worked example, exact rational
+arithmetic, closed forms, invariants or a library routine (numpy.convolve).
+"""
+from __future__ import annotations
+
+import itertools
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def load_closed_form():
+    rows = []
+    with open(os.path.join(GOLDEN, "closed_form_a05_b1_L8.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            t, h = line.split()
+            rows.append((int(t), float(h)))
+    return rows
+
+
+# ---- P1: the a = 0.5, b = 1, length-8 worked example -----------------------
+
+def pin_closed_form_scan(orc, mutation=0):
+    """pwwt.cn section 2.3 note: a = 0.5, b = 1, L = 8, hand-computed values."""
+    rows = load_closed_form()
+    h = orc.scan_ab(np.full(8, 0.5), np.ones(8), 0.0, mutation=mutation)
+    expect = np.array([v for _, v in rows])
+    assert np.array_equal(h, expect), (h, expect)
+
+
+def pin_closed_form_full_path(orc, mutation=0):
+    """The same example through the full method: delta = 1 (no softplus),
+    A = -ln 2 so Abar = 1/2, B = x = C = 1, no skip term: y_t = h_t."""
+    rows = load_closed_form()
+    L = 8
+    one = np.ones((1, L, 1))
+    A_log = np.array([[math.log(math.log(2.0))]])
+    y, h_last = orc.selective_scan(one, one, A_log, one, one, D=None, delta_softplus=False, mutation=mutation)
+    expect = np.array([v for _, v in rows])
+    assert np.max(np.abs(y[0, :, 0] - expect)) < 1e-14, y[0, :, 0]
+    assert abs(h_last[0, 0, 0] - expect[-1]) < 1e-14
+
+
+# ---- P2: order sensitivity of the combine ---------------------------------
+
+def _exact_scan(a, b, h0=Fraction(0)):
+    """h_t = a_t h_{t-1} + b_t in exact rational arithmetic."""
+    h = Fraction(h0)
+    out = []
+    for ai, bi in zip(a, b):
+        h = Fraction(ai) * h + Fraction(bi)
+        out.append(h)
+    return out
+
+
+def pin_order_sensitivity(orc, mutation=0):
+    """pwwt.cn section 2.1: the combine is order sensitive.  A constant
+    sequence cannot show a swap, so use a = (1/2, 1/4), b = (1, 2): h_2 = 2.25
+    (absorbing the input before the decay would give 0.5*... and 2.0-style
+    values instead)."""
+    h = orc.scan_ab(np.array([0.5, 0.25]), np.array([1.0, 2.0]), 0.0, mutation=mutation)
+    assert np.array_equal(h, np.array([1.0, 2.25])), h
+    # a cycling through {1, 1/2, 1/4} with small integer b: exact in fp64 at this length
+    a = [Fraction(1), Fraction(1, 2), Fraction(1, 4)] * 4
+    b = [3, -1, 2, 5, 0, -4, 1, 1, 2, -3, 7, 1]
+    ex = [float(v) for v in _exact_scan(a, b)]
+    got = orc.scan_ab(np.array([float(v) for v in a]), np.array(b, dtype=float), 0.0, mutation=mutation)
+    assert np.array_equal(got, np.array(ex)), (got, ex)
+
+
+# ---- P3: brute-force unrolled sums ----------------------------------------
+
+def pin_bruteforce_scan(orc, mutation=0):
+    """h_t = sum_{s<=t} (prod_{r=s+1..t} a_r) b_s (the unrolled recurrence),
+    evaluated by brute force; exact for dyadic inputs, 1e-13 for real ones."""
+    rng = np.random.default_rng(7)
+    for L in (1, 2, 5, 12):
+        a = [Fraction(int(k), 8) for k in rng.integers(0, 9, size=L)]
+        b = [Fraction(int(k), 8) for k in rng.integers(-16, 17, size=L)]
+        brute = []
+        for t in range(L):
+            acc = Fraction(0)
+            for s in range(t + 1):
+                p = Fraction(1)
+                for rr in range(s + 1, t + 1):
+                    p *= a[rr]
+                acc += p * b[s]
+            brute.append(float(acc))
+        got = orc.scan_ab(np.array([float(v) for v in a]), np.array([float(v) for v in b]), 0.0, mutation=mutation)
+        assert np.array_equal(got, np.array(brute)), (L, got, brute)
+    L = 64
+    a = rng.uniform(0.0, 1.0, size=L)
+    b = rng.standard_normal(L)
+    logs = np.concatenate([[0.0], np.cumsum(np.log(a))])
+    brute = np.array([sum(math.exp(logs[t + 1] - logs[s + 1]) * b[s] for s in range(t + 1)) for t in range(L)])
+    got = orc.scan_ab(a, b, 0.0, mutation=mutation)
+    assert np.max(np.abs(got - brute) / np.maximum(np.abs(brute), 1.0)) < 1e-13
+
+
+# ---- P4: associativity ----------------------------------------------------
+
+def _combine(p, q):
+    """(a1, b1) then (a2, b2) = (a1*a2, a2*b1 + b2) (pwwt.cn section 2.1)."""
+    return (p[0] * q[0], q[0] * p[1] + q[1])
+
+
+def _bracketings(items):
+    if len(items) == 1:
+        yield items[0]
+        return
+    for k in range(1, len(items)):
+        for left in _bracketings(items[:k]):
+            for right in _bracketings(items[k:]):
+                yield _combine(left, right)
+
+
+def pin_associativity(orc, mutation=0):
+    """pwwt.cn section 2.1: composition of the affine steps is associative, so
+    every bracketing of the pairs gives the serial result (bitwise for dyadic
+    pairs; the final b component is h_L from h_0 = 0)."""
+    rng = np.random.default_rng(11)
+    for L in (2, 3, 5, 7):
+        a = [float(k) / 4 for k in rng.integers(0, 5, size=L)]
+        b = [float(k) / 4 for k in rng.integers(-8, 9, size=L)]
+        h = orc.scan_ab(np.array(a), np.array(b), 0.0, mutation=mutation)
+        pairs = list(zip(a, b))
+        n = 0
+        for agg in _bracketings(pairs):
+            n += 1
+            assert agg[1] == h[-1], (L, agg, h[-1])
+        assert n == math.comb(2 * (L - 1), L - 1) // L
+
+
+# ---- P5: identity element and padding --------------------------------------
+
+def _rand_problem(rng, nb, L, nd, N, bias=-4.0):
+    x = rng.standard_normal((nb, L, nd))
+    delta = 0.5 * rng.standard_normal((nb, L, nd)) + bias
+    A_log = np.log(np.arange(1, N + 1, dtype=float))[None, :].repeat(nd, 0) + 0.1 * rng.standard_normal((nd, N))
+    B = rng.standard_normal((nb, L, N))
+    C = rng.standard_normal((nb, L, N))
+    D = rng.standard_normal(nd)
+    return x, delta, A_log, B, C, D
+
+
+def pin_identity_and_padding(orc, mutation=0):
+    """pwwt.cn section 2.3 (padding as the identity (1, 0)) and section 5.2
+    (a padded batch must match single-sequence inference)."""
+    # (1, 0) is a two-sided identity of the recurrence
+    rng = np.random.default_rng(5)
+    a = rng.uniform(0, 1, 6)
+    b = rng.standard_normal(6)
+    base = orc.scan_ab(a, b, 0.0, mutation=mutation)
+    padded = orc.scan_ab(np.concatenate([a, np.ones(3)]), np.concatenate([b, np.zeros(3)]), 0.0, mutation=mutation)
+    assert np.array_equal(padded[:6], base) and np.all(padded[6:] == base[-1])
+
+    nb, L, nd, N = 3, 40, 16, 4
+    x, delta, A_log, B, C, D = _rand_problem(rng, nb, L, nd, N)
+    vl = np.array([40, 17, 0], dtype=np.int32)
+    # garbage in the padding must not matter
+    xg, dg, Bg, Cg = x.copy(), delta.copy(), B.copy(), C.copy()
+    for bi, l in enumerate(vl):
+        xg[bi, l:] = np.nan
+        dg[bi, l:] = np.inf
+        Bg[bi, l:] = np.nan
+        Cg[bi, l:] = -np.inf
+    y, h = orc.selective_scan(x, delta, A_log, B, C, D, valid_len=vl, mutation=mutation)
+    yg, hg = orc.selective_scan(xg, dg, A_log, Bg, Cg, D, valid_len=vl, mutation=mutation)
+    assert np.array_equal(y, yg) and np.array_equal(h, hg)
+    for bi, l in enumerate(vl):
+        if l > 0:
+            y1, h1 = orc.selective_scan(x[bi:bi + 1, :l], delta[bi:bi + 1, :l], A_log, B[bi:bi + 1, :l],
+                                        C[bi:bi + 1, :l], D, mutation=mutation)
+            assert np.array_equal(y[bi, :l], y1[0]), bi
+            assert np.array_equal(h[bi], h1[0]), bi
+        else:
+            assert np.all(h[bi] == 0.0)
+        tail = y[bi, l:]
+        assert np.all(tail == 0.0) and not np.any(np.signbit(tail)), "padded y must be +0.0"
+    # out-of-range lengths clamp into [0, L]
+    y2, h2 = orc.selective_scan(x, delta, A_log, B, C, D, valid_len=np.array([L + 5, L, L], np.int32),
+                                mutation=mutation)
+    y3, h3 = orc.selective_scan(x, delta, A_log, B, C, D, valid_len=None, mutation=mutation)
+    assert np.array_equal(y2, y3) and np.array_equal(h2, h3)
+    y4, h4 = orc.selective_scan(x, delta, A_log, B, C, D, valid_len=np.array([-3, 0, 0], np.int32),
+                                mutation=mutation)
+    assert np.all(y4 == 0.0) and np.all(h4 == 0.0)
+
+
+# ---- P6: degenerate cases ----------------------------------------------------
+
+def pin_degenerate(orc, mutation=0):
+    """a = 1: h = cumsum(b); b = 0: h = 0; a = 0: h = b; B = 0 or C = 0: y = D*x."""
+    rng = np.random.default_rng(3)
+    b = rng.integers(-50, 50, size=30).astype(float)
+    assert np.array_equal(orc.scan_ab(np.ones(30), b, 0.0, mutation=mutation), np.cumsum(b))
+    assert np.array_equal(orc.scan_ab(rng.uniform(0, 1, 30), np.zeros(30), 0.0, mutation=mutation), np.zeros(30))
+    assert np.array_equal(orc.scan_ab(np.zeros(30), b, 0.0, mutation=mutation), b)
+    nb, L, nd, N = 2, 24, 8, 4
+    x, delta, A_log, B, C, D = _rand_problem(rng, nb, L, nd, N)
+    y, h = orc.selective_scan(x, delta, A_log, np.zeros_like(B), C, D, mutation=mutation)
+    assert np.array_equal(y, D[None, None, :] * x) and np.all(h == 0.0)
+    yc, hc = orc.selective_scan(x, delta, A_log, B, np.zeros_like(C), D, mutation=mutation)
+    _, href = orc.selective_scan(x, delta, A_log, B, C, D, mutation=mutation)
+    assert np.array_equal(yc, D[None, None, :] * x) and np.array_equal(hc, href)
+
+
+# ---- P7: the time-invariant case is a causal convolution --------------------
+
+def pin_lti_convolution(orc, mutation=0):
+    """pwwt.cn section 1.2: with delta, B and C constant over time the SSM is a
+    causal convolution of x with K_j = sum_n C_n Abar_n^j delta B_n,
+    Abar_n = exp(delta A_n) (checked with numpy.convolve)."""
+    rng = np.random.default_rng(13)
+    nb, L, nd, N = 2, 64, 8, 4
+    x = rng.standard_normal((nb, L, nd))
+    draw = 0.5 * rng.standard_normal(nd) - 2.0
+    delta = np.broadcast_to(draw[None, None, :], (nb, L, nd)).copy()
+    A_log = np.log(np.arange(1, N + 1, dtype=float))[None, :].repeat(nd, 0) + 0.2 * rng.standard_normal((nd, N))
+    Bc = rng.standard_normal((nb, N))
+    Cc = rng.standard_normal((nb, N))
+    B = np.broadcast_to(Bc[:, None, :], (nb, L, N)).copy()
+    C = np.broadcast_to(Cc[:, None, :], (nb, L, N)).copy()
+    y, _ = orc.selective_scan(x, delta, A_log, B, C, None, mutation=mutation)
+    sp = np.log1p(np.exp(draw))  # softplus of a moderate value
+    A = -np.exp(A_log)
+    j = np.arange(L)
+    for bi in range(nb):
+        for d in range(nd):
+            abar = np.exp(sp[d] * A[d])
+            K = np.sum(Cc[bi][None, :] * abar[None, :] ** j[:, None] * sp[d] * Bc[bi][None, :], axis=1)
+            ref = np.convolve(x[bi, :, d], K)[:L]
+            err = np.max(np.abs(y[bi, :, d] - ref)) / max(np.max(np.abs(ref)), 1e-30)
+            assert err < 1e-12, (bi, d, err)
+
+
+# ---- P8: softplus ------------------------------------------------------------
+
+def pin_softplus(orc, mutation=0):
+    """softplus(v) = log(1 + e^v): softplus(0) = ln 2, ~v for large v, ~e^v for
+    very negative v (the series e^v - e^2v/2 + e^3v/3 there).  Read through the full path: one step, Abar = 1
+    (A_log = -1000 so A = -0), B = x = C = 1, no skip term, so y_0 = delta."""
+    cases = [(0.0, math.log(2.0)), (30.0, 30.0 + math.exp(-30.0)), (-30.0, math.exp(-30.0) - math.exp(-60.0) / 2 + math.exp(-90.0) / 3),
+             (100.0, 100.0), (-5.0, math.log1p(math.exp(-5.0)))]
+    for v, expect in cases:
+        assert abs(orc.softplus(v, mutation=mutation) - expect) <= 1e-15 * abs(expect)
+        one = np.ones((1, 1, 1))
+        y, _ = orc.selective_scan(one, np.full((1, 1, 1), v), np.array([[-1000.0]]), one, one, None,
+                                  mutation=mutation)
+        assert abs(y[0, 0, 0] - expect) <= 2e-15 * abs(expect), (v, y[0, 0, 0], expect)
+
+
+# ---- P9: splitting the sequence and carrying the state -----------------------
+
+def pin_split_invariance(orc, mutation=0):
+    """bjdmk.com.cn section 4.2 / pwwt.cn section 4.2: running [0, T) and then
+    [T, L) from the carried state equals one run over [0, L), bitwise."""
+    rng = np.random.default_rng(17)
+    nb, L, nd, N, T = 2, 50, 8, 4, 19
+    x, delta, A_log, B, C, D = _rand_problem(rng, nb, L, nd, N)
+    y, h = orc.selective_scan(x, delta, A_log, B, C, D, mutation=mutation)
+    y1, h1 = orc.selective_scan(x[:, :T], delta[:, :T], A_log, B[:, :T], C[:, :T], D, mutation=mutation)
+    y2, h2 = orc.selective_scan(x[:, T:], delta[:, T:], A_log, B[:, T:], C[:, T:], D, h0=h1, mutation=mutation)
+    assert np.array_equal(np.concatenate([y1, y2], axis=1), y) and np.array_equal(h2, h)
+
+
+# ---- full method against its unrolled closed form -----------------------------
+
+def pin_bruteforce_full(orc, mutation=0):
+    """y_t = sum_n C_tn sum_{s<=t} exp(A_n * sum_{r=s+1..t} delta_r) delta_s B_sn x_s
+    + D x_t (the unrolled form, with the exponent of a sum instead of a product
+    of exponentials), brute force on tiny random inputs, with and without the
+    delta clip."""
+    rng = np.random.default_rng(19)
+    nb, L, nd, N = 2, 9, 3, 3
+    x, delta, A_log, B, C, D = _rand_problem(rng, nb, L, nd, N, bias=-1.0)
+    for clamp in (None, (0.05, 0.4)):
+        y, h = orc.selective_scan(x, delta, A_log, B, C, D, delta_clamp=clamp, mutation=mutation)
+        sp = np.logaddexp(0.0, delta)
+        if clamp is not None:
+            sp = np.clip(sp, clamp[0], clamp[1])
+        A = -np.exp(A_log)
+        for bi, d in itertools.product(range(nb), range(nd)):
+            for t in range(L):
+                acc = 0.0
+                hs = np.zeros(N)
+                for s in range(t + 1):
+                    decay = np.exp(A[d] * np.sum(sp[bi, s + 1:t + 1, d]))
+                    hs += decay * sp[bi, s, d] * B[bi, s] * x[bi, s, d]
+                acc = float(np.dot(C[bi, t], hs)) + D[d] * x[bi, t, d]
+                assert abs(y[bi, t, d] - acc) <= 1e-12 * max(1.0, abs(acc)), (bi, t, d, y[bi, t, d], acc)
+            assert np.max(np.abs(h[bi, d] - hs)) <= 1e-12 * max(1.0, np.max(np.abs(hs)))
+
+
+ALL_PINS = {
+    "closed_form_scan": pin_closed_form_scan,
+    "closed_form_full_path": pin_closed_form_full_path,
+    "order_sensitivity": pin_order_sensitivity,
+    "bruteforce_scan": pin_bruteforce_scan,
+    "associativity": pin_associativity,
+    "identity_and_padding": pin_identity_and_padding,
+    "degenerate": pin_degenerate,
+    "lti_convolution": pin_lti_convolution,
+    "softplus": pin_softplus,
+    "split_invariance": pin_split_invariance,
+    "bruteforce_full": pin_bruteforce_full,
+}
+
+# The planted mistakes (see ssm_oracle.c) and the pins expected to notice each.
+MUTATIONS = {
+    1: ("input absorbed before the decay", {"closed_form_scan", "order_sensitivity", "bruteforce_scan"}),
+    2: ("readout before the state update", {"closed_form_full_path", "bruteforce_full"}),
+    3: ("sign of A dropped", {"closed_form_full_path", "lti_convolution", "bruteforce_full"}),
+    4: ("skip term dropped", {"degenerate", "bruteforce_full"}),
+    5: ("softplus skipped", {"softplus", "lti_convolution", "bruteforce_full"}),
+    6: ("delta missing from the input term", {"lti_convolution", "bruteforce_full"}),
+    7: ("padding resets the state", {"identity_and_padding"}),
+    8: ("B and C swapped in the input term", {"bruteforce_full"}),
+}
