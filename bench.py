@@ -1,0 +1,187 @@
+#!/usr/bin/env python3
+"""Selective-scan forward benchmark on one MI355X.
+
+A step is one call of the fused forward (every step of the method: softplus,
+discretisation, the scan with its chunk carry, readout, final state) over one
+batch of seeded synthetic input already resident in HBM.  The default workload
+is the headline one: batch 8, L 4096, dim 1024, dstate 16, bf16 I/O with fp32
+arithmetic.  Three copies of the inputs are rotated so that the 256 MB
+Infinity Cache cannot serve x and delta from a previous step.
+
+Prints one JSON line on stdout: throughput in state updates per second
+(batch * L * dim * dstate per step, valid steps only for padded batches), the
+algorithmic HBM GB/s, a roofline object for the kernel, and the CPU oracle
+timed on this host on the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+if HERE not in sys.path:
+    sys.path.insert(0, HERE)
+
+METRIC = "selective-scan state-updates/s (B·L·D·N) + HBM GB/s, B8 L4096 D1024 N16 bf16"
+
+# MI355X figures used for the roofline.
+CUS, SIMDS, LANES, CLOCK_HZ = 256, 4, 16, 2.4e9
+VALU_SLOTS_PER_S = CUS * SIMDS * LANES * CLOCK_HZ      # 39.3 T lane-instructions/s (non-packed fp32)
+VALU_PEAK_TFLOPS = 2 * VALU_SLOTS_PER_S / 1e12           # 78.6 TFLOP/s fp32 FMA (packed fp32 disabled)
+HBM_PEAK_GBPS = 8000.0
+
+# Algorithmic VALU work, in issue slots (v_exp_f32 / v_log_f32 run at half the
+# fp32 FMA rate on gfx950, i.e. 2 slots each):
+#   per state update: exp(delta*A) 2 + mul delta*A 1 + mul u*B 1 + fma h 1 + fma y 1
+#   per (b, t, d):    softplus (mul, exp, add, log, mul, max, add) 9 + u = delta*x 1 + fma D*x 1
+SLOTS_PER_UPDATE = 6.0
+SLOTS_PER_ROW_STEP = 11.0
+
+
+def algorithmic_bytes(w, e: int) -> int:
+    """Bytes the method must move: x, delta read and y written ([B,L,D] each),
+    B and C read ([B,L,N] each), A_log and D read, h_last written."""
+    bld = w.batch * w.seqlen * w.dim
+    bln = w.batch * w.seqlen * w.dstate
+    return 3 * bld * e + 2 * bln * e + w.dim * w.dstate * 4 + w.dim * 4 + w.batch * w.dim * w.dstate * 4
+
+
+def algorithmic_flops(w, valid_steps: int) -> float:
+    """FMA-equivalent FLOPs (2 per VALU issue slot) of the algorithmic work."""
+    slots = valid_steps * w.dim * (w.dstate * SLOTS_PER_UPDATE + SLOTS_PER_ROW_STEP)
+    return 2.0 * slots
+
+
+def cpu_baseline(inp, w, threads: int) -> dict:
+    import oracle
+    oracle.build()
+    t0 = time.perf_counter()
+    oracle.selective_scan(inp["x"], inp["delta"], inp["A_log"], inp["B"], inp["C"], inp["D"],
+                          valid_len=inp["valid_len"], delta_clamp=w.delta_clamp, nthreads=threads)
+    dt = time.perf_counter() - t0
+    steps = w.batch * w.seqlen if inp["valid_len"] is None else int(np.sum(inp["valid_len"]))
+    upd = steps * w.dim * w.dstate
+    return {"value": upd / dt, "unit": "state-updates/s", "cores": threads, "kind": "oracle",
+            "sample": f"the whole {w.name} workload once ({upd} state updates, {dt:.2f} s wall, "
+                      f"{threads} threads over (b, d) rows; fp64, -O2)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=2, help="workload index (default: the headline one)")
+    ap.add_argument("--rotate", type=int, default=3, help="input copies rotated between steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (default: min(16, cpus))")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the scan has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import selective_state_space_scan_amd as ssm
+    from selective_state_space_scan_amd import inputs as I
+
+    if not torch.cuda.is_available():
+        print("no GPU available", file=sys.stderr)
+        return 1
+    w = I.WORKLOADS[args.workload]
+    inp = I.make_inputs(w, I.seed_for(args.workload))
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dt = torch.bfloat16 if w.io == "bf16" else torch.float32
+    sets = []
+    base = {k: torch.from_numpy(inp[k]).to(dev).to(dt).contiguous() for k in ("x", "delta", "B", "C")}
+    for r in range(max(1, args.rotate)):
+        s = {k: (v if r == 0 else v.clone()) for k, v in base.items()}
+        sets.append(s)
+    A_log = torch.from_numpy(inp["A_log"]).to(dev)
+    D = torch.from_numpy(inp["D"]).to(dev)
+    vl = None if inp["valid_len"] is None else torch.from_numpy(inp["valid_len"]).to(dev)
+    ys = [torch.empty_like(base["x"]) for _ in sets]
+    hs = [torch.empty((w.batch, w.dim, w.dstate), dtype=torch.float32, device=dev) for _ in sets]
+
+    def step(k: int):
+        s = sets[k % len(sets)]
+        ssm.selective_scan_fwd(s["x"], s["delta"], A_log, s["B"], s["C"], D, vl, delta_clamp=w.delta_clamp,
+                               y=ys[k % len(sets)], h_last=hs[k % len(sets)])
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        step(k)
+        ev[k][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    ms_per_step = total_ms / args.steps
+    kern_avg_ms = float(np.mean(kern_ms))
+
+    steps_valid = w.batch * w.seqlen if inp["valid_len"] is None else int(np.sum(inp["valid_len"]))
+    updates = steps_valid * w.dim * w.dstate
+    e = 2 if w.io == "bf16" else 4
+    nbytes = algorithmic_bytes(w, e)
+    flops = algorithmic_flops(w, steps_valid)
+    gbps = nbytes / (kern_avg_ms * 1e-3) / 1e9
+    tflops = flops / (kern_avg_ms * 1e-3) / 1e12
+    t_alu = flops / (VALU_PEAK_TFLOPS * 1e12)
+    t_hbm = nbytes / (HBM_PEAK_GBPS * 1e9)
+    bound = "alu" if t_alu >= t_hbm else "hbm"
+    roof = ({"bound": "alu", "achieved": round(tflops, 3), "peak": round(VALU_PEAK_TFLOPS, 2), "unit": "TFLOP/s",
+             "frac": round(tflops / VALU_PEAK_TFLOPS, 4), "traffic": None}
+            if bound == "alu" else
+            {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+             "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None})
+    roof["kernel"] = "ssm_fwd_kernel"
+    roof["kernel_avg_ms"] = round(kern_avg_ms, 5)
+    roof["hbm_gbps"] = round(gbps, 1)
+    roof["hbm_frac"] = round(gbps / HBM_PEAK_GBPS, 4)
+    roof["algorithmic_bytes"] = nbytes
+    roof["algorithmic_tflop"] = flops / 1e12
+
+    out = {
+        "metric": METRIC,
+        "value": updates / (ms_per_step * 1e-3),
+        "unit": "state-updates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "hbm_gbps": round(nbytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim, "dstate": w.dstate,
+                   "io": w.io, "state_updates_per_step": updates, "input_copies_rotated": len(sets)},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        threads = args.cpu_threads or min(16, os.cpu_count() or 1)
+        out["cpu_baseline"] = cpu_baseline(inp, w, threads)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,108 @@
+/*
+ * ssm_scan.h -- C ABI of the MI355X (gfx950) fused selective-scan forward.
+ *
+ * The operation (Mamba's selective state-space scan, forward only).  For every
+ * batch row b, channel d and state n, with A = -exp(A_log[d,n]):
+ *
+ *     delta_t = softplus(delta_raw[b,t,d])            (optional; then optional clip)
+ *     Abar_t  = exp(delta_t * A)                      in (0, 1)
+ *     h_t     = Abar_t * h_{t-1} + delta_t * B[b,t,n] * x[b,t,d],   h_{-1} = 0
+ *     y[b,t,d] = sum_n C[b,t,n] * h_t[n] + D[d] * x[b,t,d]
+ *     h_last[b,d,n] = h after the last valid step of row b
+ *
+ * Sources: the recurrence and readout are those of the pwwt.cn article
+ * (section 1.1, "the recursion"); the parameterisation A = -exp(A_log),
+ * softplus(delta) > 0 and Abar = exp(delta*A) is its section 2.4; the clip of
+ * delta after softplus is its section 3.3; padding folded in as the identity
+ * pair (a, b) = (1, 0) is its section 2.3; the state after the last step is
+ * what the chunked scan of the bjdmk.com.cn article (section 4.2) carries out.
+ * The input term is delta*B*x (not the exact zero-order-hold B), and B and C
+ * are shared by all channels of a batch row.
+ *
+ * Layouts (all row-major, contiguous, no strides):
+ *   x, delta, y : [batch, seqlen, dim]       io dtype (fp32 or bf16), dim fastest
+ *   B, C        : [batch, seqlen, dstate]    io dtype, dstate fastest
+ *   A_log       : [dim, dstate]              fp32
+ *   D           : [dim]                      fp32, may be NULL (no skip term)
+ *   valid_len   : [batch]                    int32, may be NULL (every row has seqlen steps)
+ *   h_last      : [batch, dim, dstate]       fp32, may be NULL (not written)
+ * Every pointer is a device pointer on the handle's device.  The caller owns
+ * all memory; the library allocates nothing per call.
+ *
+ * Padding: steps t >= valid_len[b] are the identity (the state is carried
+ * unchanged), y there is written as +0.0, and the values of x, delta, B and C
+ * there never reach any output (NaN or Inf included).  valid_len outside
+ * [0, seqlen] is clamped into it.  Padding is on the right only.
+ *
+ * Arithmetic is fp32 throughout (bf16 inputs convert exactly); y is rounded to
+ * the io dtype with round-to-nearest-even.  Results are bitwise reproducible
+ * run to run for the same inputs and dims.
+ *
+ * Errors: every entry point returns SSM_OK (0) or a negative SSM_ERR_* code and
+ * never throws.  Argument checks happen on the host before anything is
+ * enqueued; a failed check enqueues nothing.
+ */
+#ifndef SSM_SCAN_H
+#define SSM_SCAN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ssm_scan_handle_s* ssm_scan_t;
+
+enum ssm_io_dtype { SSM_IO_F32 = 0, SSM_IO_BF16 = 1 };
+
+enum ssm_status {
+  SSM_OK = 0,
+  SSM_ERR_INVALID_ARG = -1,     /* NULL required pointer or handle, negative dim, bad flag or clip bounds */
+  SSM_ERR_UNSUPPORTED = -2,     /* dstate not 16/32/64, dim not a multiple of 16, misaligned pointer, wrong GPU */
+  SSM_ERR_ALIAS = -3,           /* y or h_last overlaps an input, or y overlaps h_last */
+  SSM_ERR_HIP = -4,             /* a HIP runtime or launch error */
+  SSM_ERR_NO_DEVICE = -5,       /* no usable GPU at the requested ordinal */
+  SSM_ERR_DEVICE_MISMATCH = -6  /* the calling thread's current device is not the handle's device */
+};
+
+typedef struct ssm_scan_dims {
+  int64_t batch;          /* number of rows b */
+  int64_t seqlen;         /* L (the padded length when valid_len is given); 0 is a valid no-op */
+  int64_t dim;            /* D channels: multiple of 16 */
+  int64_t dstate;         /* N states per channel: 16, 32 or 64 */
+  int32_t io_dtype;       /* enum ssm_io_dtype for x, delta, B, C and y */
+  int32_t delta_softplus; /* 1: delta = softplus(delta_raw); 0: delta is used as given */
+  int32_t delta_clamp;    /* 1: delta = min(max(delta, delta_min), delta_max) after softplus */
+  float delta_min;        /* used when delta_clamp = 1; must satisfy 0 <= delta_min <= delta_max */
+  float delta_max;
+} ssm_scan_dims;
+
+/* Create a handle bound to GPU `device_ordinal` (HIP numbering).  Loads nothing
+ * lazily later: after this returns SSM_OK the handle is immutable, so one
+ * handle may serve concurrent calls on different streams.  *out is set to NULL
+ * on failure.  Errors: SSM_ERR_INVALID_ARG (out NULL), SSM_ERR_NO_DEVICE,
+ * SSM_ERR_UNSUPPORTED (not a gfx950 device), SSM_ERR_HIP. */
+int ssm_scan_create(ssm_scan_t* out, int device_ordinal);
+
+/* Enqueue the forward on `stream` (a hipStream_t; NULL = the default stream)
+ * and return without waiting.  The calling thread's current device must be the
+ * handle's device.  Inputs must stay valid and unmodified, and outputs
+ * untouched, until the stream reaches the end of this work.  Pointer
+ * alignment: natural for the element type.  batch == 0, dim == 0 or
+ * seqlen == 0 are valid (for seqlen == 0, h_last is written with zeros). */
+int ssm_selective_scan_fwd(ssm_scan_t handle, const void* x, const void* delta, const float* A_log, const void* B,
+                           const void* C, const float* D, const int32_t* valid_len, void* y, float* h_last,
+                           const ssm_scan_dims* dims, void* stream);
+
+/* Release the handle.  NULL is accepted.  The caller must ensure no work
+ * enqueued with the handle is still to be launched. */
+int ssm_scan_destroy(ssm_scan_t handle);
+
+/* A static, human-readable string for a status code (never NULL). */
+const char* ssm_scan_error_string(int code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSM_SCAN_H */

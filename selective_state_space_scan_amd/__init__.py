@@ -1,0 +1,18 @@
+"""Fused selective state-space scan forward for MI355X (gfx950).
+
+The scan itself runs in the HIP library ``libssmscan.so`` behind the C ABI of
+``include/ssm_scan.h``; this package is its thin binding (``selective_scan_fwd``
+and the raw ``ssm_*`` calls), the build script and the seeded synthetic input
+generators.
+"""
+from ._binding import (EXPORTED, SSM_ERR_ALIAS, SSM_ERR_DEVICE_MISMATCH, SSM_ERR_HIP, SSM_ERR_INVALID_ARG,
+                       SSM_ERR_NO_DEVICE, SSM_ERR_UNSUPPORTED, SSM_IO_BF16, SSM_IO_F32, SSM_OK, SsmScanError,
+                       error_string, lib, library_path, selective_scan_fwd, ssm_scan_create, ssm_scan_destroy,
+                       ssm_scan_dims, ssm_selective_scan_fwd)
+
+__all__ = [
+    "selective_scan_fwd", "ssm_scan_create", "ssm_scan_destroy", "ssm_selective_scan_fwd", "ssm_scan_dims",
+    "SsmScanError", "error_string", "lib", "library_path", "EXPORTED", "SSM_OK", "SSM_ERR_INVALID_ARG",
+    "SSM_ERR_UNSUPPORTED", "SSM_ERR_ALIAS", "SSM_ERR_HIP", "SSM_ERR_NO_DEVICE", "SSM_ERR_DEVICE_MISMATCH",
+    "SSM_IO_F32", "SSM_IO_BF16",
+]

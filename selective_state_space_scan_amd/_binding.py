@@ -1,0 +1,196 @@
+"""ctypes binding of the C ABI in ``include/ssm_scan.h`` (argument marshalling only).
+
+Every step of the scan runs in the HIP library; this module checks tensor
+shapes, dtypes and devices, allocates outputs with torch, and passes raw device
+pointers and the current HIP stream across the ABI.  There is no fallback: if
+the library is missing or no GPU is usable, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+from .build import LIB_PATH
+
+SSM_OK = 0
+SSM_ERR_INVALID_ARG = -1
+SSM_ERR_UNSUPPORTED = -2
+SSM_ERR_ALIAS = -3
+SSM_ERR_HIP = -4
+SSM_ERR_NO_DEVICE = -5
+SSM_ERR_DEVICE_MISMATCH = -6
+
+SSM_IO_F32 = 0
+SSM_IO_BF16 = 1
+
+# Names declared in include/ssm_scan.h.
+EXPORTED = ("ssm_scan_create", "ssm_selective_scan_fwd", "ssm_scan_destroy", "ssm_scan_error_string")
+
+
+class SsmScanError(RuntimeError):
+    def __init__(self, code: int, what: str):
+        super().__init__(f"{what}: {error_string(code)} ({code})")
+        self.code = code
+
+
+class ssm_scan_dims(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int64),
+        ("seqlen", ctypes.c_int64),
+        ("dim", ctypes.c_int64),
+        ("dstate", ctypes.c_int64),
+        ("io_dtype", ctypes.c_int32),
+        ("delta_softplus", ctypes.c_int32),
+        ("delta_clamp", ctypes.c_int32),
+        ("delta_min", ctypes.c_float),
+        ("delta_max", ctypes.c_float),
+    ]
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def library_path() -> str:
+    return LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Load ``libssmscan.so`` (built in-tree by ``build.build()``); raise if absent."""
+    global _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(
+                f"HIP library not built: {LIB_PATH} is missing; run "
+                "`python -m selective_state_space_scan_amd.build` (or __graft_entry__.build())")
+        L = ctypes.CDLL(LIB_PATH)
+        vp = ctypes.c_void_p
+        L.ssm_scan_create.argtypes = [ctypes.POINTER(vp), ctypes.c_int]
+        L.ssm_scan_create.restype = ctypes.c_int
+        L.ssm_scan_destroy.argtypes = [vp]
+        L.ssm_scan_destroy.restype = ctypes.c_int
+        L.ssm_scan_error_string.argtypes = [ctypes.c_int]
+        L.ssm_scan_error_string.restype = ctypes.c_char_p
+        L.ssm_selective_scan_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                             ctypes.POINTER(ssm_scan_dims), vp]
+        L.ssm_selective_scan_fwd.restype = ctypes.c_int
+        _lib = L
+        return L
+
+
+def error_string(code: int) -> str:
+    return lib().ssm_scan_error_string(int(code)).decode()
+
+
+# ---- raw C ABI (pointers as ints) ------------------------------------------
+
+def ssm_scan_create(device_ordinal: int) -> int:
+    h = ctypes.c_void_p()
+    rc = lib().ssm_scan_create(ctypes.byref(h), int(device_ordinal))
+    if rc != SSM_OK:
+        raise SsmScanError(rc, "ssm_scan_create")
+    return h.value
+
+
+def ssm_scan_destroy(handle: int | None) -> None:
+    rc = lib().ssm_scan_destroy(handle)
+    if rc != SSM_OK:
+        raise SsmScanError(rc, "ssm_scan_destroy")
+
+
+def ssm_selective_scan_fwd(handle, x, delta, A_log, B, C, D, valid_len, y, h_last, dims: ssm_scan_dims,
+                           stream) -> int:
+    """Calls the C entry point with raw pointers (ints or None); returns the status code."""
+    return lib().ssm_selective_scan_fwd(handle, x, delta, A_log, B, C, D, valid_len, y, h_last,
+                                        ctypes.byref(dims), stream)
+
+
+# ---- torch front end -----------------------------------------------------
+
+_handles: dict[int, int] = {}
+_handles_lock = threading.Lock()
+
+
+def handle_for(device_index: int) -> int:
+    with _handles_lock:
+        h = _handles.get(device_index)
+        if h is None:
+            h = ssm_scan_create(device_index)
+            _handles[device_index] = h
+        return h
+
+
+def selective_scan_fwd(x, delta, A_log, B, C, D=None, valid_len=None, *, delta_softplus: bool = True,
+                       delta_clamp=None, y=None, h_last=None, return_h_last: bool = True, stream=None):
+    """Selective-scan forward on the GPU.  Returns ``(y, h_last)``.
+
+    x, delta: [batch, L, dim]; B, C: [batch, L, dstate]; all four the same dtype
+    (torch.float32 or torch.bfloat16).  A_log: [dim, dstate] float32.  D: [dim]
+    float32 or None.  valid_len: [batch] int32 or None.  delta_clamp: None or
+    (min, max), applied after softplus.  Outputs are allocated unless given:
+    y like x, h_last [batch, dim, dstate] float32 (None if return_h_last is
+    False and no h_last is given).  The call is asynchronous on ``stream``
+    (default: the current stream of x's device).
+    """
+    import torch
+
+    if x.device.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    dev = x.device
+    io = {torch.float32: SSM_IO_F32, torch.bfloat16: SSM_IO_BF16}.get(x.dtype)
+    if io is None:
+        raise TypeError("x must be float32 or bfloat16")
+    if x.dim() != 3:
+        raise ValueError("x must be [batch, L, dim]")
+    nb, L, nd = x.shape
+    if A_log.dim() != 2 or A_log.shape[0] != nd:
+        raise ValueError("A_log must be [dim, dstate]")
+    N = A_log.shape[1]
+    for name, t, shape, dt in (("delta", delta, (nb, L, nd), x.dtype), ("B", B, (nb, L, N), x.dtype),
+                               ("C", C, (nb, L, N), x.dtype), ("A_log", A_log, (nd, N), torch.float32)):
+        if tuple(t.shape) != shape or t.dtype != dt or t.device != dev:
+            raise ValueError(f"{name} must be {shape} {dt} on {dev}, got {tuple(t.shape)} {t.dtype} on {t.device}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if not x.is_contiguous():
+        raise ValueError("x must be contiguous")
+    if D is not None and (tuple(D.shape) != (nd,) or D.dtype != torch.float32 or D.device != dev
+                          or not D.is_contiguous()):
+        raise ValueError("D must be a contiguous [dim] float32 tensor on x's device")
+    if valid_len is not None and (tuple(valid_len.shape) != (nb,) or valid_len.dtype != torch.int32
+                                  or valid_len.device != dev or not valid_len.is_contiguous()):
+        raise ValueError("valid_len must be a contiguous [batch] int32 tensor on x's device")
+    if y is None:
+        y = torch.empty_like(x)
+    elif tuple(y.shape) != (nb, L, nd) or y.dtype != x.dtype or y.device != dev or not y.is_contiguous():
+        raise ValueError("y must be a contiguous tensor like x")
+    if h_last is None and return_h_last:
+        h_last = torch.empty((nb, nd, N), dtype=torch.float32, device=dev)
+    elif h_last is not None and (tuple(h_last.shape) != (nb, nd, N) or h_last.dtype != torch.float32
+                                 or h_last.device != dev or not h_last.is_contiguous()):
+        raise ValueError("h_last must be a contiguous [batch, dim, dstate] float32 tensor")
+
+    dims = ssm_scan_dims()
+    dims.batch, dims.seqlen, dims.dim, dims.dstate = nb, L, nd, N
+    dims.io_dtype = io
+    dims.delta_softplus = 1 if delta_softplus else 0
+    if delta_clamp is not None:
+        dims.delta_clamp = 1
+        dims.delta_min, dims.delta_max = float(delta_clamp[0]), float(delta_clamp[1])
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+    def ptr(t):
+        return None if t is None or t.numel() == 0 else t.data_ptr()
+
+    with torch.cuda.device(dev):
+        h = handle_for(dev.index if dev.index is not None else torch.cuda.current_device())
+        rc = ssm_selective_scan_fwd(h, ptr(x), ptr(delta), ptr(A_log), ptr(B), ptr(C), ptr(D), ptr(valid_len),
+                                    ptr(y), ptr(h_last), dims, sptr)
+    if rc != SSM_OK:
+        raise SsmScanError(rc, "ssm_selective_scan_fwd")
+    return y, h_last

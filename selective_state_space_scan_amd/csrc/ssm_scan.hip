@@ -1,0 +1,602 @@
+// Fused selective-scan forward for MI355X (gfx950, CDNA4) and its C ABI.
+//
+// The method (the pwwt.cn article, sections 1.1, 2.1-2.4 and 3.1; the
+// bjdmk.com.cn article, sections 2.2-2.4): for each batch row b, channel d and
+// state n the diagonal recurrence h_t = exp(delta_t*A[d,n]) h_{t-1} +
+// delta_t B[b,t,n] x[b,t,d] is an affine map h -> a*h + b per step.  Affine
+// maps compose associatively, (a1,b1) then (a2,b2) = (a1*a2, a2*b1 + b2), so
+// the time axis can be cut into pieces that are folded independently and then
+// joined by carrying the state from piece to piece.
+//
+// Work mapping (one workgroup = one batch row x 16 consecutive channels):
+//  * A lane owns one channel and 16 states (dstate = 16*G; lane row r of the
+//    wave picks the state group g = r % G) and K consecutive time steps (the
+//    time sub-chunk q = r / G of the wave).  A tile of the time axis is
+//    SUB = W*(4/G) sub-chunks of K steps.
+//  * Pass 1 (per lane, serial over K steps): Abar = exp2(delta*A*log2e) for
+//    each state, kept in registers; the sub-chunk's pair
+//    (a_prod, b_total) = (exp2(A*log2e*sum(delta)), folded b) goes to LDS.
+//  * Carry walk: one lane per (channel, state) walks the SUB pairs of the tile
+//    in time order, leaving each sub-chunk's incoming state in LDS and keeping
+//    the carry in a register from tile to tile (the serial chunk-to-chunk
+//    carry of the chunked scan).
+//  * Pass 2 (per lane, serial over K steps): h = Abar*h + delta*B*x from the
+//    incoming state using the cached Abar (so each state update costs exactly
+//    one exp), y = C.h + D*x.
+//  * B and C are shared by the 16 channels of a workgroup: lane s of each
+//    16-lane row holds B[b,t,16g+s] (and C) for that row's step, and the
+//    per-state operand is taken with a DPP row broadcast (row_newbcast:s) fused
+//    into the multiply, so no LDS staging or per-lane conversion is needed for
+//    them.
+//  * Padded steps (t >= valid_len) get delta = 0, u = 0 and B = 0, i.e. the
+//    identity pair (1, 0) (pwwt.cn section 2.3, identity element instead of a
+//    branch), and y = +0 there.  Tiles that lie wholly in the padding are not
+//    loaded at all.
+//  * With G > 1 the 16-state partial sums of y from the G state-group rows are
+//    added with v_permlane16_swap / v_permlane32_swap in a fixed order.
+//
+// All arithmetic is fp32; exp is v_exp_f32 (2^x) after a log2(e) prescale.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+#include <new>
+
+#include "ssm_scan.h"
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+struct FwdParams {
+  const void* x;
+  const void* delta;
+  const float* A_log;
+  const void* B;
+  const void* C;
+  const float* D;
+  const int32_t* valid_len;
+  void* y;
+  float* h_last;
+  int64_t L;
+  int32_t nb;
+  int32_t nd;
+  int32_t n_cg;  // channel groups of 16 per batch row
+  int32_t softplus;
+  int32_t clamp;
+  float dmin;
+  float dmax;
+};
+
+// ---- element access ------------------------------------------------------
+
+template <typename IO>
+struct Elem;
+
+template <>
+struct Elem<float> {
+  static __device__ __forceinline__ float load(const void* p, int64_t i) {
+    return __builtin_nontemporal_load(static_cast<const float*>(p) + i);
+  }
+  static __device__ __forceinline__ float load_cached(const void* p, int64_t i) {
+    return static_cast<const float*>(p)[i];
+  }
+  static __device__ __forceinline__ void store(void* p, int64_t i, float v) {
+    __builtin_nontemporal_store(v, static_cast<float*>(p) + i);
+  }
+};
+
+// bf16 is carried as its 16-bit pattern; widening to fp32 is exact.
+template <>
+struct Elem<uint16_t> {
+  static __device__ __forceinline__ float load(const void* p, int64_t i) {
+    const uint32_t u = __builtin_nontemporal_load(static_cast<const uint16_t*>(p) + i);
+    return __builtin_bit_cast(float, u << 16);
+  }
+  static __device__ __forceinline__ float load_cached(const void* p, int64_t i) {
+    const uint32_t u = static_cast<const uint16_t*>(p)[i];
+    return __builtin_bit_cast(float, u << 16);
+  }
+  static __device__ __forceinline__ void store(void* p, int64_t i, float v) {
+    // v_cvt_pk_bf16_f32: round to nearest even.
+    const __bf16 h = static_cast<__bf16>(v);
+    __builtin_nontemporal_store(__builtin_bit_cast(uint16_t, h), static_cast<uint16_t*>(p) + i);
+  }
+};
+
+// ---- math ----------------------------------------------------------------
+
+__device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
+
+// softplus(v) = max(v, 0) + log1p(exp(-|v|)).  log1p(e) is evaluated as
+// log(w) * e / (w - 1) with w = 1 + e, the correction that makes log(1 + e)
+// accurate for small e (D. Goldberg, "What every computer scientist should know
+// about floating-point arithmetic", 1991, theorem 4); when w rounds to 1,
+// log1p(e) = e to working precision.
+__device__ __forceinline__ float softplus_f32(float v) {
+  const float e = fast_exp2(-__builtin_fabsf(v) * kLog2e);
+  const float w = 1.0f + e;
+  const float wm1 = w - 1.0f;
+  const float lg = __builtin_amdgcn_logf(w) * kLn2;  // v_log_f32 is log2
+  const float l1p = (wm1 == 0.0f) ? e : lg * (e * __builtin_amdgcn_rcpf(wm1));
+  return __builtin_fmaxf(v, 0.0f) + l1p;
+}
+
+// DPP row_newbcast:S -- every lane of a 16-lane row reads lane S of that row.
+template <int S>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + S, 0xf, 0xf, true));
+}
+
+// y0..y3 += C[s] * h[s] over the 16 states, C[s] taken from lane s of the
+// row by DPP row_newbcast fused into v_fmac_f32 (the compiler does not fuse a
+// DPP move into v_fmac, so this is written out).  The leading s_nop covers the
+// DPP hazards (a VALU write of the DPP source needs 2 wait states before the
+// read, a VALU write of EXEC needs 5); c is not written inside the block.
+__device__ __forceinline__ void dot16_row_bcast(float& y0, float& y1, float& y2, float& y3, float c,
+                                                const float (&h)[16]) {
+  asm volatile(
+      "s_nop 4\n\t"
+      "v_fmac_f32_dpp %0, %4, %5 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %4, %6 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %4, %7 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %4, %8 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %4, %9 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %4, %10 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %4, %11 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %4, %12 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %4, %13 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %4, %14 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %4, %15 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %4, %16 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %4, %17 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %4, %18 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %4, %19 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %4, %20 row_newbcast:15 row_mask:0xf bank_mask:0xf"
+      : "+v"(y0), "+v"(y1), "+v"(y2), "+v"(y3)
+      : "v"(c), "v"(h[0]), "v"(h[1]), "v"(h[2]), "v"(h[3]), "v"(h[4]), "v"(h[5]), "v"(h[6]), "v"(h[7]),
+        "v"(h[8]), "v"(h[9]), "v"(h[10]), "v"(h[11]), "v"(h[12]), "v"(h[13]), "v"(h[14]), "v"(h[15]));
+}
+
+// Sum of v over the G state-group rows that share a time sub-chunk; every lane
+// of those rows gets the same bits (fixed order: (r0 + r1) + (r2 + r3)).
+// v_permlane16_swap exchanges rows 0<->1 and 2<->3 between its two operands,
+// v_permlane32_swap the two 32-lane halves; starting both operands from the
+// same value leaves each lane with its own value and its partner's.  Written
+// out because the compiler folds the builtin's two results into one when both
+// operands are the same value.  s_nop 1 covers the VALU-write -> permlane-read
+// hazard.
+template <int G>
+__device__ __forceinline__ float sum_state_groups(float v) {
+  if constexpr (G == 1) {
+    return v;
+  } else {
+    float a = v, b = v;
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    float s = a + b;
+    if constexpr (G == 4) {
+      float c = s, d = s;
+      asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(c), "+v"(d));
+      s = c + d;
+    }
+    return s;
+  }
+}
+
+template <int S, int K>
+struct Unroll {
+  template <typename F>
+  static __device__ __forceinline__ void run(F&& f) {
+    f.template operator()<S>();
+    Unroll<S + 1, K>::run(f);
+  }
+};
+template <int K>
+struct Unroll<K, K> {
+  template <typename F>
+  static __device__ __forceinline__ void run(F&&) {}
+};
+
+// ---- the kernel ----------------------------------------------------------
+
+template <typename IO, int G, int K, int W, bool SOFTPLUS, bool CLAMP>
+__global__ __launch_bounds__(64 * W) void ssm_fwd_kernel(FwdParams p) {
+  constexpr int N = 16 * G;             // states per channel
+  constexpr int QR = 4 / G;             // time sub-chunks per wave
+  constexpr int SUB = W * QR;           // sub-chunks per tile
+  constexpr int T = SUB * K;            // steps per tile
+  constexpr int NS = N + 4;             // padded LDS row (channel) stride in floats
+  constexpr int PAIRS = 16 * N;         // (channel, state) pairs of the workgroup
+  constexpr int NT = 64 * W;            // threads
+  constexpr int PPL = (PAIRS + NT - 1) / NT;
+
+  __shared__ float agg_a[SUB * 16 * NS];
+  __shared__ float agg_b[SUB * 16 * NS];  // b_total, then overwritten with the incoming state
+
+  // Workgroup -> (batch row, channel group).  Workgroups are dealt to the 8
+  // XCDs round-robin; consecutive logical ids are kept on one XCD so that
+  // neighbouring channel groups (which share 128-byte lines of x, delta and y)
+  // share that XCD's L2.
+  const int64_t total = static_cast<int64_t>(p.nb) * p.n_cg;
+  const int64_t bid = blockIdx.x;
+  const int64_t per_xcd = total / 8;
+  const int64_t logical = (bid < per_xcd * 8) ? (bid % 8) * per_xcd + bid / 8 : bid;
+  const int b = static_cast<int>(logical / p.n_cg);
+  const int cg = static_cast<int>(logical % p.n_cg);
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int r = lane >> 4;
+  const int c = lane & 15;
+  const int q = r / G;
+  const int g = r % G;
+  const int j = w * QR + q;  // sub-chunk index within the tile
+  const int d = cg * 16 + c;
+  const int64_t L = p.L;
+  const int nd = p.nd;
+
+  int64_t len = L;
+  if (p.valid_len != nullptr) {
+    const int64_t v = p.valid_len[b];
+    len = v < 0 ? 0 : (v > L ? L : v);
+  }
+
+  float A2[16];
+#pragma unroll
+  for (int s = 0; s < 16; ++s) A2[s] = -expf(p.A_log[static_cast<int64_t>(d) * N + 16 * g + s]) * kLog2e;
+  const float dskip = (p.D != nullptr) ? p.D[d] : 0.0f;
+
+  float carry[PPL];
+#pragma unroll
+  for (int k = 0; k < PPL; ++k) carry[k] = 0.0f;
+
+  const int64_t row_xd = static_cast<int64_t>(b) * L * nd + d;          // x/delta/y index at t = 0
+  const int64_t row_bc = static_cast<int64_t>(b) * L * N + 16 * g + c;  // B/C index at t = 0 (lane holds state 16g+c)
+  const int64_t ntiles = (L + T - 1) / T;
+  const int64_t ntiles_valid = (len + T - 1) / T;
+
+  // One tile of T steps.  FULL: every step of the tile is valid (t < len).
+  auto tile_body = [&]<bool FULL>(int64_t tile) {
+    const int64_t t0 = tile * T + static_cast<int64_t>(j) * K;
+
+    float xv[K], dv[K], bv[K], cv[K];
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      const int64_t t = t0 + i;
+      const bool ok = FULL || t < len;
+      xv[i] = ok ? Elem<IO>::load(p.x, row_xd + t * nd) : 0.0f;
+      dv[i] = ok ? Elem<IO>::load(p.delta, row_xd + t * nd) : 0.0f;
+      bv[i] = ok ? Elem<IO>::load_cached(p.B, row_bc + t * N) : 0.0f;
+      cv[i] = ok ? Elem<IO>::load_cached(p.C, row_bc + t * N) : 0.0f;
+    }
+
+    // ---- pass 1: discretise, cache Abar, fold the sub-chunk ----
+    float ab[K][16];
+    float u[K];
+    float bt[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) bt[s] = 0.0f;
+    float sd = 0.0f;
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      float dl = dv[i];
+      if constexpr (SOFTPLUS) dl = softplus_f32(dl);
+      if constexpr (CLAMP) dl = __builtin_amdgcn_fmed3f(dl, p.dmin, p.dmax);
+      if constexpr (!FULL) dl = (t0 + i < len) ? dl : 0.0f;  // padded step: delta = 0 -> Abar = 1
+      u[i] = dl * xv[i];
+      sd += dl;
+      const float bi = bv[i];
+      const float ui = u[i];
+      Unroll<0, 16>::run([&]<int S>() {
+        ab[i][S] = fast_exp2(dl * A2[S]);
+        bt[S] = __builtin_fmaf(ab[i][S], bt[S], row_bcast<S>(bi) * ui);
+      });
+    }
+
+    __syncthreads();  // the previous tile's pass 2 has read its incoming states
+    {
+      float* pa = agg_a + (j * 16 + c) * NS + 16 * g;
+      float* pb = agg_b + (j * 16 + c) * NS + 16 * g;
+#pragma unroll
+      for (int s = 0; s < 16; s += 4) {
+        *reinterpret_cast<float4*>(pa + s) =
+            make_float4(fast_exp2(A2[s] * sd), fast_exp2(A2[s + 1] * sd), fast_exp2(A2[s + 2] * sd),
+                        fast_exp2(A2[s + 3] * sd));
+        *reinterpret_cast<float4*>(pb + s) = make_float4(bt[s], bt[s + 1], bt[s + 2], bt[s + 3]);
+      }
+    }
+    __syncthreads();
+
+    // ---- carry walk over the tile's sub-chunks, in time order ----
+#pragma unroll
+    for (int k = 0; k < PPL; ++k) {
+      const int pr = tid + k * NT;
+      if (PAIRS % NT == 0 || pr < PAIRS) {
+        const int cc = pr / N;
+        const int n = pr % N;
+        float cr = carry[k];
+#pragma unroll 4
+        for (int jj = 0; jj < SUB; ++jj) {
+          const int idx = (jj * 16 + cc) * NS + n;
+          const float a = agg_a[idx];
+          const float bb = agg_b[idx];
+          agg_b[idx] = cr;
+          cr = __builtin_fmaf(a, cr, bb);
+        }
+        carry[k] = cr;
+      }
+    }
+    __syncthreads();
+
+    // ---- pass 2: states from the incoming state, readout ----
+    float h[16];
+    {
+      const float* pb = agg_b + (j * 16 + c) * NS + 16 * g;
+#pragma unroll
+      for (int s = 0; s < 16; s += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(pb + s);
+        h[s] = v.x;
+        h[s + 1] = v.y;
+        h[s + 2] = v.z;
+        h[s + 3] = v.w;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      // A fresh name for B so that its broadcasts are not shared with pass 1
+      // (sharing would keep 16 broadcast copies live across the carry walk).
+      float bi = bv[i];
+      asm volatile("" : "+v"(bi));
+      const float ui = u[i];
+      float y0 = 0.0f, y1 = 0.0f, y2 = 0.0f, y3 = 0.0f;
+      Unroll<0, 16>::run([&]<int S>() { h[S] = __builtin_fmaf(ab[i][S], h[S], row_bcast<S>(bi) * ui); });
+      dot16_row_bcast(y0, y1, y2, y3, cv[i], h);
+      float yv = sum_state_groups<G>((y0 + y1) + (y2 + y3));
+      yv = __builtin_fmaf(dskip, xv[i], yv);
+      const int64_t t = t0 + i;
+      if constexpr (FULL) {
+        if (G == 1 || (i % G) == g) Elem<IO>::store(p.y, row_xd + t * nd, yv);
+      } else {
+        if (t >= len) yv = 0.0f;
+        if (t < L && (G == 1 || (i % G) == g)) Elem<IO>::store(p.y, row_xd + t * nd, yv);
+      }
+    }
+  };
+
+  for (int64_t tile = 0; tile < ntiles; ++tile) {
+    if (tile >= ntiles_valid) {
+      // Whole tile is padding: the carry is unchanged and y is +0.
+      const int64_t t0 = tile * T + static_cast<int64_t>(j) * K;
+#pragma unroll
+      for (int i = 0; i < K; ++i) {
+        const int64_t t = t0 + i;
+        if (t < L && (G == 1 || (i % G) == g)) Elem<IO>::store(p.y, row_xd + t * nd, 0.0f);
+      }
+    } else if ((tile + 1) * T <= len) {
+      tile_body.template operator()<true>(tile);
+    } else {
+      tile_body.template operator()<false>(tile);
+    }
+  }
+
+  if (p.h_last != nullptr) {
+#pragma unroll
+    for (int k = 0; k < PPL; ++k) {
+      const int pr = tid + k * NT;
+      if (PAIRS % NT == 0 || pr < PAIRS) {
+        const int cc = pr / N;
+        const int n = pr % N;
+        p.h_last[(static_cast<int64_t>(b) * nd + cg * 16 + cc) * N + n] = carry[k];
+      }
+    }
+  }
+}
+
+// ---- launch configuration ------------------------------------------------
+
+template <typename IO, int G>
+struct Config;
+// dstate 16: 8 waves, 4 steps per lane -> 128-step tiles.
+template <typename IO>
+struct Config<IO, 1> {
+  static constexpr int K = 4, W = 8;
+};
+// dstate 32: 8 waves, 4 steps per lane -> 64-step tiles.
+template <typename IO>
+struct Config<IO, 2> {
+  static constexpr int K = 4, W = 8;
+};
+// dstate 64: 8 waves, 4 steps per lane -> 32-step tiles.
+template <typename IO>
+struct Config<IO, 4> {
+  static constexpr int K = 4, W = 8;
+};
+
+template <typename IO, int G, bool SP, bool CL>
+hipError_t launch_flags(const FwdParams& prm, hipStream_t stream) {
+  constexpr int K = Config<IO, G>::K, W = Config<IO, G>::W;
+  const int64_t blocks = static_cast<int64_t>(prm.nb) * prm.n_cg;
+  hipLaunchKernelGGL((ssm_fwd_kernel<IO, G, K, W, SP, CL>), dim3(static_cast<unsigned>(blocks)), dim3(64 * W), 0,
+                     stream, prm);
+  return hipGetLastError();
+}
+
+template <typename IO, int G>
+hipError_t launch(const FwdParams& prm, hipStream_t stream) {
+  if (prm.softplus)
+    return prm.clamp ? launch_flags<IO, G, true, true>(prm, stream) : launch_flags<IO, G, true, false>(prm, stream);
+  return prm.clamp ? launch_flags<IO, G, false, true>(prm, stream) : launch_flags<IO, G, false, false>(prm, stream);
+}
+
+template <typename IO>
+hipError_t launch_io(int G, const FwdParams& prm, hipStream_t stream) {
+  switch (G) {
+    case 1:
+      return launch<IO, 1>(prm, stream);
+    case 2:
+      return launch<IO, 2>(prm, stream);
+    default:
+      return launch<IO, 4>(prm, stream);
+  }
+}
+
+// Zero-fills h_last when there are no time steps.
+__global__ void zero_fill_kernel(float* p, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.0f;
+}
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+}  // namespace
+
+struct ssm_scan_handle_s {
+  int device;
+  int cu_count;
+};
+
+extern "C" {
+
+int ssm_scan_create(ssm_scan_t* out, int device_ordinal) {
+  if (out == nullptr) return SSM_ERR_INVALID_ARG;
+  *out = nullptr;
+  int count = 0;
+  if (hipGetDeviceCount(&count) != hipSuccess) {
+    (void)hipGetLastError();
+    return SSM_ERR_NO_DEVICE;
+  }
+  if (device_ordinal < 0 || device_ordinal >= count) return SSM_ERR_NO_DEVICE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device_ordinal) != hipSuccess) {
+    (void)hipGetLastError();
+    return SSM_ERR_HIP;
+  }
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return SSM_ERR_UNSUPPORTED;
+  ssm_scan_handle_s* h = new (std::nothrow) ssm_scan_handle_s;
+  if (h == nullptr) return SSM_ERR_HIP;
+  h->device = device_ordinal;
+  h->cu_count = prop.multiProcessorCount;
+  *out = h;
+  return SSM_OK;
+}
+
+int ssm_scan_destroy(ssm_scan_t handle) {
+  delete handle;
+  return SSM_OK;
+}
+
+const char* ssm_scan_error_string(int code) {
+  switch (code) {
+    case SSM_OK:
+      return "ok";
+    case SSM_ERR_INVALID_ARG:
+      return "invalid argument (null pointer or handle, negative size, bad flag or clip bounds)";
+    case SSM_ERR_UNSUPPORTED:
+      return "unsupported (dstate not 16/32/64, dim not a multiple of 16, misaligned pointer, or not gfx950)";
+    case SSM_ERR_ALIAS:
+      return "an output overlaps an input or the other output";
+    case SSM_ERR_HIP:
+      return "HIP runtime or launch error";
+    case SSM_ERR_NO_DEVICE:
+      return "no usable GPU at that ordinal";
+    case SSM_ERR_DEVICE_MISMATCH:
+      return "the current device is not the handle's device";
+    default:
+      return "unknown status code";
+  }
+}
+
+// Checks run in this order: dims, sizes and flags; pointers; alignment;
+// aliasing; the handle; the current device.  Nothing is enqueued unless all
+// pass.
+int ssm_selective_scan_fwd(ssm_scan_t handle, const void* x, const void* delta, const float* A_log, const void* B,
+                           const void* C, const float* D, const int32_t* valid_len, void* y, float* h_last,
+                           const ssm_scan_dims* dims, void* stream) {
+  if (dims == nullptr) return SSM_ERR_INVALID_ARG;
+  const int64_t nb = dims->batch, L = dims->seqlen, nd = dims->dim, N = dims->dstate;
+  if (nb < 0 || L < 0 || nd < 0 || N < 0) return SSM_ERR_INVALID_ARG;
+  if (dims->io_dtype != SSM_IO_F32 && dims->io_dtype != SSM_IO_BF16) return SSM_ERR_INVALID_ARG;
+  if (dims->delta_softplus != 0 && dims->delta_softplus != 1) return SSM_ERR_INVALID_ARG;
+  if (dims->delta_clamp != 0 && dims->delta_clamp != 1) return SSM_ERR_INVALID_ARG;
+  if (dims->delta_clamp == 1 && !(dims->delta_min >= 0.0f && dims->delta_min <= dims->delta_max &&
+                                  dims->delta_max < __builtin_inff()))
+    return SSM_ERR_INVALID_ARG;
+  if (N != 16 && N != 32 && N != 64) return SSM_ERR_UNSUPPORTED;
+  if (nd % 16 != 0) return SSM_ERR_UNSUPPORTED;
+  // Grid and index limits: one workgroup per (row, 16 channels); element
+  // indices are 64-bit in the kernel.
+  if (nb > 0 && nd > 0 && (nb * (nd / 16) > 0x7fffffffLL || nb > 0x7fffffffLL || nd > 0x7fffffffLL))
+    return SSM_ERR_UNSUPPORTED;
+  if (L > 0 && nb > 0 && nd > 0 && L > (int64_t{1} << 62) / (nb * nd * (N > nd ? N : nd)))
+    return SSM_ERR_UNSUPPORTED;
+
+  const bool empty = (nb == 0 || nd == 0);
+  const size_t e = dims->io_dtype == SSM_IO_BF16 ? 2 : 4;
+  const size_t n_xd = static_cast<size_t>(nb) * L * nd, n_bc = static_cast<size_t>(nb) * L * N;
+  if (!empty) {
+    if (A_log == nullptr) return SSM_ERR_INVALID_ARG;
+    if (L > 0 && (x == nullptr || delta == nullptr || B == nullptr || C == nullptr || y == nullptr))
+      return SSM_ERR_INVALID_ARG;
+    if (!aligned(x, e) || !aligned(delta, e) || !aligned(B, e) || !aligned(C, e) || !aligned(y, e) ||
+        !aligned(A_log, 4) || !aligned(D, 4) || !aligned(valid_len, 4) || !aligned(h_last, 4))
+      return SSM_ERR_UNSUPPORTED;
+    const size_t by = L > 0 ? n_xd * e : 0, bh = h_last ? static_cast<size_t>(nb) * nd * N * 4 : 0;
+    const void* ins[] = {x, delta, B, C, A_log, D, valid_len};
+    const size_t ins_n[] = {n_xd * e, n_xd * e, n_bc * e, n_bc * e, static_cast<size_t>(nd) * N * 4,
+                            D ? static_cast<size_t>(nd) * 4 : 0, valid_len ? static_cast<size_t>(nb) * 4 : 0};
+    for (int k = 0; k < 7; ++k) {
+      if (overlaps(y, by, ins[k], ins_n[k]) || overlaps(h_last, bh, ins[k], ins_n[k])) return SSM_ERR_ALIAS;
+    }
+    if (overlaps(y, by, h_last, bh)) return SSM_ERR_ALIAS;
+  }
+  if (handle == nullptr) return SSM_ERR_INVALID_ARG;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) {
+    (void)hipGetLastError();
+    return SSM_ERR_HIP;
+  }
+  if (cur != handle->device) return SSM_ERR_DEVICE_MISMATCH;
+  if (empty) return SSM_OK;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (L == 0) {
+    if (h_last == nullptr) return SSM_OK;
+    const int64_t n = nb * nd * N;
+    hipLaunchKernelGGL(zero_fill_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, h_last, n);
+    return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+  }
+
+  FwdParams prm;
+  prm.x = x;
+  prm.delta = delta;
+  prm.A_log = A_log;
+  prm.B = B;
+  prm.C = C;
+  prm.D = D;
+  prm.valid_len = valid_len;
+  prm.y = y;
+  prm.h_last = h_last;
+  prm.L = L;
+  prm.nb = static_cast<int32_t>(nb);
+  prm.nd = static_cast<int32_t>(nd);
+  prm.n_cg = static_cast<int32_t>(nd / 16);
+  prm.softplus = dims->delta_softplus;
+  prm.clamp = dims->delta_clamp;
+  prm.dmin = dims->delta_min;
+  prm.dmax = dims->delta_max;
+  const int G = static_cast<int>(N / 16);
+  const hipError_t err =
+      dims->io_dtype == SSM_IO_BF16 ? launch_io<uint16_t>(G, prm, s) : launch_io<float>(G, prm, s);
+  return err == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+}  // extern "C"

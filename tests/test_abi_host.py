@@ -1,0 +1,125 @@
+"""The C ABI library on the host (no GPU needed): it loads, exports every
+function declared in include/ssm_scan.h, and rejects bad arguments with the
+documented codes before touching the GPU (argument checks precede the handle
+check, so a NULL handle reaches them)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import selective_state_space_scan_amd as ssm
+
+REPO = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    src = open(os.path.join(REPO, "include", "ssm_scan.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssm_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_function():
+    names = declared_functions()
+    assert set(names) == set(ssm.EXPORTED), names
+    lib = ctypes.CDLL(ssm.library_path())
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_error_strings():
+    for code in (0, -1, -2, -3, -4, -5, -6, -99, 5):
+        s = ssm.error_string(code)
+        assert isinstance(s, str) and s
+
+
+def _dims(**kw):
+    d = ssm.ssm_scan_dims()
+    d.batch, d.seqlen, d.dim, d.dstate = kw.get("batch", 2), kw.get("seqlen", 8), kw.get("dim", 16), kw.get("dstate", 16)
+    d.io_dtype = kw.get("io", ssm.SSM_IO_BF16)
+    d.delta_softplus = kw.get("softplus", 1)
+    d.delta_clamp = kw.get("clamp", 0)
+    d.delta_min, d.delta_max = kw.get("dmin", 0.0), kw.get("dmax", 0.0)
+    return d
+
+
+MB = 1 << 20
+# Fake, non-overlapping, aligned addresses: never dereferenced, since every call
+# below fails an argument check (or the NULL-handle check) first.
+PTRS = dict(x=1 * MB, delta=2 * MB, A_log=3 * MB, B=4 * MB, C=5 * MB, D=None, valid_len=None, y=6 * MB, h_last=7 * MB)
+
+
+def call(dims, **over):
+    p = dict(PTRS, **over)
+    return ssm.ssm_selective_scan_fwd(over.get("handle"), p["x"], p["delta"], p["A_log"], p["B"], p["C"], p["D"],
+                                      p["valid_len"], p["y"], p["h_last"], dims, None)
+
+
+def test_valid_arguments_reach_the_handle_check():
+    assert call(_dims()) == ssm.SSM_ERR_INVALID_ARG  # NULL handle
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(batch=-1), ssm.SSM_ERR_INVALID_ARG),
+    (dict(seqlen=-1), ssm.SSM_ERR_INVALID_ARG),
+    (dict(dim=-16), ssm.SSM_ERR_INVALID_ARG),
+    (dict(io=7), ssm.SSM_ERR_INVALID_ARG),
+    (dict(softplus=2), ssm.SSM_ERR_INVALID_ARG),
+    (dict(clamp=3), ssm.SSM_ERR_INVALID_ARG),
+    (dict(clamp=1, dmin=0.5, dmax=0.1), ssm.SSM_ERR_INVALID_ARG),
+    (dict(clamp=1, dmin=-1.0, dmax=0.1), ssm.SSM_ERR_INVALID_ARG),
+    (dict(dstate=8), ssm.SSM_ERR_UNSUPPORTED),
+    (dict(dstate=17), ssm.SSM_ERR_UNSUPPORTED),
+    (dict(dim=24), ssm.SSM_ERR_UNSUPPORTED),
+])
+def test_bad_dims(kw, code):
+    assert call(_dims(**kw)) == code
+
+
+def test_null_dims():
+    lib = ssm.lib()
+    assert lib.ssm_selective_scan_fwd(None, 1, 2, 3, 4, 5, None, None, 6, None, None, None) == ssm.SSM_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("name", ["x", "delta", "A_log", "B", "C", "y"])
+def test_null_required_pointer(name):
+    assert call(_dims(), **{name: None}) == ssm.SSM_ERR_INVALID_ARG
+
+
+def test_misaligned_pointers():
+    assert call(_dims(io=ssm.SSM_IO_BF16), x=1 * MB + 1) == ssm.SSM_ERR_UNSUPPORTED
+    assert call(_dims(io=ssm.SSM_IO_F32), x=1 * MB + 2) == ssm.SSM_ERR_UNSUPPORTED
+    assert call(_dims(), A_log=3 * MB + 2) == ssm.SSM_ERR_UNSUPPORTED
+    assert call(_dims(), h_last=7 * MB + 2) == ssm.SSM_ERR_UNSUPPORTED
+
+
+def test_aliasing():
+    assert call(_dims(), y=PTRS["x"]) == ssm.SSM_ERR_ALIAS
+    assert call(_dims(), y=PTRS["B"] + 2) == ssm.SSM_ERR_ALIAS
+    assert call(_dims(), h_last=PTRS["A_log"]) == ssm.SSM_ERR_ALIAS
+    assert call(_dims(), h_last=PTRS["y"]) == ssm.SSM_ERR_ALIAS
+    # adjacent but disjoint ranges are fine (y = 2*8*16*2 bytes below h_last)
+    assert call(_dims(), y=7 * MB - 2 * 8 * 16 * 2) == ssm.SSM_ERR_INVALID_ARG
+
+
+def test_empty_problem_needs_only_the_handle():
+    assert call(_dims(batch=0), x=None, delta=None, B=None, C=None, y=None, A_log=None) == ssm.SSM_ERR_INVALID_ARG
+
+
+def test_create_without_gpu_fails_cleanly():
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    with pytest.raises(ssm.SsmScanError) as ei:
+        ssm.ssm_scan_create(0)
+    assert ei.value.code in (ssm.SSM_ERR_NO_DEVICE, ssm.SSM_ERR_HIP)
+    lib = ssm.lib()
+    assert lib.ssm_scan_create(None, 0) == ssm.SSM_ERR_INVALID_ARG
+    assert lib.ssm_scan_destroy(None) == ssm.SSM_OK
+
+
+def test_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 8, 16)
+    with pytest.raises(ValueError):
+        ssm.selective_scan_fwd(x, x, torch.zeros(16, 16), torch.zeros(1, 8, 16), torch.zeros(1, 8, 16))

@@ -1,0 +1,146 @@
+"""Bit-exact valid-length handling, determinism and concurrent streams (needs the GPU)."""
+import numpy as np
+import pytest
+
+from gpu_util import run_gpu, to_device, to_np64
+from selective_state_space_scan_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+
+def _bits(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).cpu().numpy()
+    return t.view(torch.int32).cpu().numpy()
+
+
+LENGTHS = [0, 1, 3, 4, 5, 63, 64, 65, 127, 128, 129, 255, 256, 257, 600, 999, 1000]
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [16, 64])
+def test_padding_bit_exact(io, N):
+    """pwwt.cn section 2.3 / 5.2: padding is the identity and must not touch
+    the valid outputs.  y at padded steps is +0.0; garbage (NaN, Inf) in the
+    padding changes nothing; valid_len = L matches no valid_len; a padded row
+    equals the same row run alone with its own length (bitwise)."""
+    import torch
+    L = 1000
+    base = I.WORKLOADS[0] if io == "f32" else I.WORKLOADS[3]
+    w = I.small_workload(base, batch=len(LENGTHS), seqlen=L, dim=32)
+    w = type(w)(**{**w.__dict__, "dstate": N, "varlen_lo": None})
+    inp = I.make_inputs(w, 31337 + N)
+    inp["valid_len"] = np.array(LENGTHS, np.int32)
+    dev = to_device(inp, io)
+    y, h = run_gpu(dev)
+    yb, hb = _bits(y), _bits(h)
+    for b, l in enumerate(LENGTHS):
+        assert np.all(yb[b, l:] == 0), f"row {b}: padded y must be +0.0 bits"
+    # garbage in the padding
+    garb = {k: dev[k].clone() for k in ("x", "delta", "B", "C")}
+    for b, l in enumerate(LENGTHS):
+        garb["x"][b, l:] = float("nan")
+        garb["delta"][b, l:] = float("inf")
+        garb["B"][b, l:] = float("nan")
+        garb["C"][b, l:] = float("-inf")
+    y2, h2 = run_gpu(dict(dev, **garb))
+    assert np.array_equal(_bits(y2), yb) and np.array_equal(_bits(h2), hb)
+    # each row alone, truncated to its length
+    for b, l in enumerate(LENGTHS):
+        if l == 0:
+            assert np.all(to_np64(h[b]) == 0.0)
+            continue
+        one = {k: dev[k][b:b + 1, :l].contiguous() for k in ("x", "delta", "B", "C")}
+        one.update(A_log=dev["A_log"], D=dev["D"], valid_len=None)
+        y1, h1 = run_gpu(one)
+        assert np.array_equal(_bits(y1)[0], yb[b, :l]), f"row {b} (len {l}): y differs from the row run alone"
+        assert np.array_equal(_bits(h1)[0], hb[b]), f"row {b} (len {l}): h_last differs"
+    # valid_len all = L vs none; and out-of-range lengths clamp
+    full = dict(dev, valid_len=torch.full((w.batch,), L, dtype=torch.int32, device=y.device))
+    over = dict(dev, valid_len=torch.full((w.batch,), L + 7, dtype=torch.int32, device=y.device))
+    none = dict(dev, valid_len=None)
+    r_full, r_over, r_none = run_gpu(full), run_gpu(over), run_gpu(none)
+    assert np.array_equal(_bits(r_full[0]), _bits(r_none[0])) and np.array_equal(_bits(r_full[1]), _bits(r_none[1]))
+    assert np.array_equal(_bits(r_over[0]), _bits(r_none[0])) and np.array_equal(_bits(r_over[1]), _bits(r_none[1]))
+    neg = dict(dev, valid_len=torch.full((w.batch,), -5, dtype=torch.int32, device=y.device))
+    yn, hn = run_gpu(neg)
+    assert np.all(_bits(yn) == 0) and np.all(_bits(hn) == 0)
+
+
+def test_config3_lengths_bit_exact_rows():
+    """The variable-length workload recipe (lengths uniform in [128, 8192]) at
+    reduced width: each padded row equals that row run alone, bitwise."""
+    w = I.small_workload(I.WORKLOADS[3], batch=6, seqlen=8192, dim=16)
+    inp = I.make_inputs(w, I.seed_for(3) + 7)
+    dev = to_device(inp, w.io)
+    y, h = run_gpu(dev)
+    for b in range(w.batch):
+        l = int(inp["valid_len"][b])
+        one = {k: dev[k][b:b + 1, :l].contiguous() for k in ("x", "delta", "B", "C")}
+        one.update(A_log=dev["A_log"], D=dev["D"], valid_len=None)
+        y1, h1 = run_gpu(one)
+        assert np.array_equal(_bits(y1)[0], _bits(y)[b, :l]) and np.array_equal(_bits(h1)[0], _bits(h)[b])
+        assert np.all(_bits(y)[b, l:] == 0)
+
+
+def test_determinism():
+    """pwwt.cn section 5.2: the same input twice must give the same bits."""
+    w = I.small_workload(I.WORKLOADS[2], batch=4, seqlen=2048, dim=256)
+    dev = to_device(I.make_inputs(w, 99), w.io)
+    ya, ha = run_gpu(dev)
+    ya, ha = ya.clone(), ha.clone()
+    for _ in range(3):
+        yb, hb = run_gpu(dev)
+        assert np.array_equal(_bits(ya), _bits(yb)) and np.array_equal(_bits(ha), _bits(hb))
+
+
+def test_concurrent_streams():
+    """pwwt.cn section 5.2 (sporadic errors under multi-stream concurrency):
+    two streams with different inputs give the serial results bitwise."""
+    import torch
+    import selective_state_space_scan_amd as ssm
+    w = I.small_workload(I.WORKLOADS[2], batch=4, seqlen=2048, dim=512)
+    d1 = to_device(I.make_inputs(w, 1), w.io)
+    d2 = to_device(I.make_inputs(w, 2), w.io)
+    r1 = [t.clone() for t in run_gpu(d1)]
+    r2 = [t.clone() for t in run_gpu(d2)]
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    outs = []
+    for _ in range(4):
+        with torch.cuda.stream(s1):
+            a = ssm.selective_scan_fwd(d1["x"], d1["delta"], d1["A_log"], d1["B"], d1["C"], d1["D"], None)
+        with torch.cuda.stream(s2):
+            b = ssm.selective_scan_fwd(d2["x"], d2["delta"], d2["A_log"], d2["B"], d2["C"], d2["D"], None)
+        outs.append((a, b))
+    torch.cuda.synchronize()
+    for a, b in outs:
+        assert np.array_equal(_bits(a[0]), _bits(r1[0])) and np.array_equal(_bits(a[1]), _bits(r1[1]))
+        assert np.array_equal(_bits(b[0]), _bits(r2[0])) and np.array_equal(_bits(b[1]), _bits(r2[1]))
+
+
+def test_h_last_optional_and_outputs_given():
+    import torch
+    import selective_state_space_scan_amd as ssm
+    w = I.small_workload(I.WORKLOADS[2], batch=2, seqlen=500, dim=32)
+    dev = to_device(I.make_inputs(w, 5), w.io)
+    y_ref, h_ref = run_gpu(dev)
+    y_out = torch.full_like(dev["x"], 7.0)
+    y, h = ssm.selective_scan_fwd(dev["x"], dev["delta"], dev["A_log"], dev["B"], dev["C"], dev["D"], None,
+                                  y=y_out, return_h_last=False)
+    torch.cuda.synchronize()
+    assert h is None and y is y_out and np.array_equal(_bits(y), _bits(y_ref))
+
+
+def test_seqlen_zero_writes_zero_state():
+    import torch
+    import selective_state_space_scan_amd as ssm
+    dev = torch.device("cuda:0")
+    x = torch.empty((2, 0, 32), dtype=torch.bfloat16, device=dev)
+    B = torch.empty((2, 0, 16), dtype=torch.bfloat16, device=dev)
+    A_log = torch.zeros((32, 16), device=dev)
+    h_last = torch.full((2, 32, 16), 3.0, device=dev)
+    y, h = ssm.selective_scan_fwd(x, x, A_log, B, B, None, None, h_last=h_last)
+    torch.cuda.synchronize()
+    assert y.shape == (2, 0, 32) and torch.all(h == 0)

@@ -1,0 +1,141 @@
+"""HIP path against the fp64 oracle on the same seeded inputs (needs the GPU).
+
+Tolerance (per output tensor, y and h_last separately):
+max_i |g_i - r_i| / max(|r_i|, rms(r)) <= 1e-4 for fp32 I/O, <= 2e-2 for bf16
+I/O.  Valid-length handling is checked bit for bit."""
+import numpy as np
+import pytest
+
+from conftest import rel_err
+from gpu_util import oracle_full, oracle_rows, run_gpu, to_device, to_np64, tol_for
+from selective_state_space_scan_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+
+def _check_full(w, inp, with_D=True, label=""):
+    if not with_D:
+        inp = dict(inp, D=None)
+    dev = to_device(inp, w.io)
+    y, h = run_gpu(dev, delta_clamp=w.delta_clamp)
+    yr, hr = oracle_full(inp, delta_clamp=w.delta_clamp)
+    yg, hg = to_np64(y), to_np64(h)
+    assert np.all(np.isfinite(yg)) and np.all(np.isfinite(hg))
+    mask = None
+    if inp.get("valid_len") is not None:
+        t = np.arange(w.seqlen)[None, :, None]
+        mask = np.broadcast_to(t < np.asarray(inp["valid_len"])[:, None, None], yr.shape)
+        assert np.all(yg[~mask] == 0.0)
+    ey, eh = rel_err(yg, yr, mask), rel_err(hg, hr)
+    print(f"{label} {w.name} D={with_D}: y err {ey:.3e}  h_last err {eh:.3e}  "
+          f"y max abs {np.max(np.abs(yg - yr)):.3e}", flush=True)
+    tol = tol_for(w.io)
+    assert ey <= tol and eh <= tol, (ey, eh)
+    return ey, eh
+
+
+@pytest.mark.parametrize("with_D", [True, False])
+def test_config0_full(with_D):
+    w = I.WORKLOADS[0]
+    _check_full(w, I.make_inputs(w, I.seed_for(0)), with_D)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+@pytest.mark.parametrize("with_D", [True, False])
+def test_configs_reduced_size(cfg, with_D):
+    """The same recipe at sizes the oracle finishes quickly: several tiles plus
+    a ragged tail (seqlen not a multiple of any tile size)."""
+    base = I.WORKLOADS[cfg]
+    w = I.small_workload(base, batch=3, seqlen=1000 if cfg != 4 else 700, dim=48)
+    if base.varlen_lo is not None:
+        w = I.small_workload(base, batch=5, seqlen=1000, dim=48)
+        w = type(w)(**{**w.__dict__, "varlen_lo": 1})
+    _check_full(w, I.make_inputs(w, I.seed_for(cfg) + 100), with_D)
+
+
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_configs_full_size_sampled(cfg):
+    """Full-size workloads in the benchmark's launch configuration, checked on
+    sampled channels (each (b, d) row the oracle computes on its own)."""
+    w = I.WORKLOADS[cfg]
+    inp = I.make_inputs(w, I.seed_for(cfg))
+    dev = to_device(inp, w.io)
+    y, h = run_gpu(dev, delta_clamp=w.delta_clamp)
+    rng = np.random.default_rng(cfg)
+    rows = {(0, 0), (w.batch - 1, w.dim - 1), (0, 15), (w.batch - 1, 16)}
+    for _ in range(20 if cfg != 4 else 10):
+        rows.add((int(rng.integers(w.batch)), int(rng.integers(w.dim))))
+    rows = sorted(rows)
+    yr, hr = oracle_rows(inp, rows, delta_clamp=w.delta_clamp, nthreads=16)
+    yg = np.stack([to_np64(y[b, :, d]) for b, d in rows])
+    hg = np.stack([to_np64(h[b, d]) for b, d in rows])
+    mask = None
+    if inp.get("valid_len") is not None:
+        vl = np.asarray(inp["valid_len"])
+        mask = np.arange(w.seqlen)[None, :] < np.array([vl[b] for b, _ in rows])[:, None]
+        assert np.all(yg[~mask] == 0.0)
+    ey, eh = rel_err(yg, yr, mask), rel_err(hg, hr)
+    print(f"{w.name} sampled {len(rows)} rows: y err {ey:.3e}  h_last err {eh:.3e}", flush=True)
+    assert np.all(np.isfinite(to_np64(y)))
+    assert ey <= tol_for(w.io) and eh <= tol_for(w.io)
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_closed_form_through_abi(io):
+    """pwwt.cn section 2.3 worked example through the C ABI: delta = 1 (no
+    softplus), A = -ln 2 (Abar = 1/2), B = x = C = 1 on every state, D absent:
+    y_t = 16 * (2 - 2^(1-t))."""
+    import math
+    L, nd, N = 8, 16, 16
+    inp = dict(x=np.ones((1, L, nd), np.float32), delta=np.ones((1, L, nd), np.float32),
+               A_log=np.full((nd, N), math.log(math.log(2.0)), np.float32),
+               B=np.ones((1, L, N), np.float32), C=np.ones((1, L, N), np.float32), D=None, valid_len=None)
+    y, h = run_gpu(to_device(inp, io), delta_softplus=False)
+    expect = np.array([2.0 - 2.0 ** (1 - t) for t in range(1, L + 1)])
+    yg = to_np64(y)[0]
+    assert np.max(np.abs(yg - 16 * expect[:, None])) <= (1e-5 if io == "f32" else 0.07)
+    assert np.max(np.abs(to_np64(h)[0] - expect[-1])) <= 1e-5
+
+
+@pytest.mark.parametrize("L", [1, 2, 3, 7, 8, 9, 31, 33, 64, 65, 127, 128, 129, 200])
+def test_fp32_short_lengths(L):
+    """pwwt.cn section 4.4: short lengths (8 to 64 and around) against the serial
+    reference, fp32 I/O; expect max abs error around 1e-5 or better."""
+    w = I.small_workload(I.WORKLOADS[0], batch=2, seqlen=L, dim=32)
+    ey, eh = _check_full(w, I.make_inputs(w, 77 + L))
+    assert ey <= 1e-4
+
+
+def test_fp32_error_trend_with_length():
+    """pwwt.cn section 4.4: the error should grow slowly from L = 256 to 8192
+    (fp32 state); a precision bug shows up as errors near 1e-1."""
+    errs = []
+    for L in (256, 1024, 4096, 8192):
+        w = I.small_workload(I.WORKLOADS[0], batch=1, seqlen=L, dim=16)
+        ey, eh = _check_full(w, I.make_inputs(w, 500 + L))
+        errs.append(max(ey, eh))
+    print("error vs L:", errs)
+    assert max(errs) <= 1e-4
+
+
+@pytest.mark.parametrize("N", [16, 32, 64])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_dstate_variants(N, io):
+    base = I.WORKLOADS[0] if io == "f32" else I.WORKLOADS[2]
+    w = I.small_workload(base, batch=2, seqlen=333, dim=32)
+    w = type(w)(**{**w.__dict__, "dstate": N})
+    _check_full(w, I.make_inputs(w, 900 + N))
+
+
+def test_delta_clamp_and_no_softplus():
+    w = I.small_workload(I.WORKLOADS[0], batch=2, seqlen=300, dim=32)
+    inp = I.make_inputs(w, 4242)
+    dev = to_device(inp, "f32")
+    y, h = run_gpu(dev, delta_clamp=(0.01, 0.05))
+    yr, hr = oracle_full(inp, delta_clamp=(0.01, 0.05))
+    assert rel_err(to_np64(y), yr) <= 1e-4 and rel_err(to_np64(h), hr) <= 1e-4
+    pos = dict(inp, delta=np.abs(inp["delta"]) * 0.01)
+    dev = to_device(pos, "f32")
+    y, h = run_gpu(dev, delta_softplus=False)
+    yr, hr = oracle_full(pos, delta_softplus=False)
+    assert rel_err(to_np64(y), yr) <= 1e-4 and rel_err(to_np64(h), hr) <= 1e-4
