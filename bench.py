@@ -80,6 +80,9 @@ def main() -> int:
     ap.add_argument("--rotate", type=int, default=3, help="input copies rotated between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (default: min(16, cpus))")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="instead of the benchmark, run a plain device copy of this many MiB three times "
+                         "(reference reading for the HBM byte counters)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -95,6 +98,15 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("no GPU available", file=sys.stderr)
         return 1
+    if args.copy_calibration_mb:
+        n = args.copy_calibration_mb << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "repeats": 3}))
+        return 0
     w = I.WORKLOADS[args.workload]
     inp = I.make_inputs(w, I.seed_for(args.workload))
     dev = torch.device("cuda:0")

@@ -14,12 +14,13 @@
 //    time sub-chunk q = r / G of the wave).  A tile of the time axis is
 //    SUB = W*(4/G) sub-chunks of K steps.
 //  * Pass 1 (per lane, serial over K steps): Abar = exp2(delta*A*log2e) for
-//    each state, kept in registers; the sub-chunk's pair
-//    (a_prod, b_total) = (exp2(A*log2e*sum(delta)), folded b) goes to LDS.
-//  * Carry walk: one lane per (channel, state) walks the SUB pairs of the tile
-//    in time order, leaving each sub-chunk's incoming state in LDS and keeping
-//    the carry in a register from tile to tile (the serial chunk-to-chunk
-//    carry of the chunked scan).
+//    each state, kept in registers; the sub-chunk's folded b_total and its
+//    sum of delta go to LDS.
+//  * Carry walk: one lane per (channel, state) walks the SUB sub-chunks of the
+//    tile in time order with the pair (a_prod, b_total), a_prod =
+//    exp2(A*log2e*sum(delta)), leaving each sub-chunk's incoming state in LDS
+//    and keeping the carry in a register from tile to tile (the serial
+//    chunk-to-chunk carry of the chunked scan).
 //  * Pass 2 (per lane, serial over K steps): h = Abar*h + delta*B*x from the
 //    incoming state using the cached Abar (so each state update costs exactly
 //    one exp), y = C.h + D*x.
@@ -71,38 +72,51 @@ struct FwdParams {
 };
 
 // ---- element access ------------------------------------------------------
+//
+// Every tensor row a workgroup touches is addressed through a buffer resource
+// (base in SGPRs) with a fixed per-lane byte offset in a VGPR and the per-step
+// offset in an SGPR, so the hot loop does no per-lane address arithmetic.  The
+// host guarantees that a row spans fewer than 2^31 bytes.
+
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+
+// Word 3 of a gfx9 buffer resource: 32-bit data format, everything else zero.
+constexpr int kRsrcWord3 = 0x00020000;
+// Cache policy bits of buffer instructions: non-temporal for data streamed once.
+constexpr int kStream = 2;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kRsrcWord3);
+}
 
 template <typename IO>
 struct Elem;
 
 template <>
 struct Elem<float> {
-  static __device__ __forceinline__ float load(const void* p, int64_t i) {
-    return __builtin_nontemporal_load(static_cast<const float*>(p) + i);
+  static constexpr int kBytes = 4;
+  template <int AUX>
+  static __device__ __forceinline__ float load(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, AUX));
   }
-  static __device__ __forceinline__ float load_cached(const void* p, int64_t i) {
-    return static_cast<const float*>(p)[i];
-  }
-  static __device__ __forceinline__ void store(void* p, int64_t i, float v) {
-    __builtin_nontemporal_store(v, static_cast<float*>(p) + i);
+  static __device__ __forceinline__ void store(rsrc_t r, uint32_t voff, uint32_t soff, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, soff, kStream);
   }
 };
 
 // bf16 is carried as its 16-bit pattern; widening to fp32 is exact.
 template <>
 struct Elem<uint16_t> {
-  static __device__ __forceinline__ float load(const void* p, int64_t i) {
-    const uint32_t u = __builtin_nontemporal_load(static_cast<const uint16_t*>(p) + i);
+  static constexpr int kBytes = 2;
+  template <int AUX>
+  static __device__ __forceinline__ float load(rsrc_t r, uint32_t voff, uint32_t soff) {
+    const uint32_t u = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, AUX);
     return __builtin_bit_cast(float, u << 16);
   }
-  static __device__ __forceinline__ float load_cached(const void* p, int64_t i) {
-    const uint32_t u = static_cast<const uint16_t*>(p)[i];
-    return __builtin_bit_cast(float, u << 16);
-  }
-  static __device__ __forceinline__ void store(void* p, int64_t i, float v) {
+  static __device__ __forceinline__ void store(rsrc_t r, uint32_t voff, uint32_t soff, float v) {
     // v_cvt_pk_bf16_f32: round to nearest even.
     const __bf16 h = static_cast<__bf16>(v);
-    __builtin_nontemporal_store(__builtin_bit_cast(uint16_t, h), static_cast<uint16_t*>(p) + i);
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, h), r, voff, soff, kStream);
   }
 };
 
@@ -130,32 +144,32 @@ __device__ __forceinline__ float row_bcast(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + S, 0xf, 0xf, true));
 }
 
-// y0..y3 += C[s] * h[s] over the 16 states, C[s] taken from lane s of the
-// row by DPP row_newbcast fused into v_fmac_f32 (the compiler does not fuse a
-// DPP move into v_fmac, so this is written out).  The leading s_nop covers the
-// DPP hazards (a VALU write of the DPP source needs 2 wait states before the
-// read, a VALU write of EXEC needs 5); c is not written inside the block.
-__device__ __forceinline__ void dot16_row_bcast(float& y0, float& y1, float& y2, float& y3, float c,
-                                                const float (&h)[16]) {
+// y0 += C[s] * h[s] (even s), y1 += C[s] * h[s] (odd s) over the 16 states,
+// C[s] taken from lane s of the row by DPP row_newbcast fused into v_fmac_f32
+// (the compiler does not fuse a DPP move into v_fmac, so this is written out).
+// The leading s_nop covers the DPP hazards (a VALU write of the DPP source
+// needs 2 wait states before the read, a VALU write of EXEC needs 5); c is not
+// written inside the block.
+__device__ __forceinline__ void dot16_row_bcast(float& y0, float& y1, float c, const float (&h)[16]) {
   asm volatile(
       "s_nop 4\n\t"
-      "v_fmac_f32_dpp %0, %4, %5 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
-      "v_fmac_f32_dpp %1, %4, %6 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
-      "v_fmac_f32_dpp %2, %4, %7 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
-      "v_fmac_f32_dpp %3, %4, %8 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
-      "v_fmac_f32_dpp %0, %4, %9 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
-      "v_fmac_f32_dpp %1, %4, %10 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
-      "v_fmac_f32_dpp %2, %4, %11 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
-      "v_fmac_f32_dpp %3, %4, %12 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
-      "v_fmac_f32_dpp %0, %4, %13 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
-      "v_fmac_f32_dpp %1, %4, %14 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
-      "v_fmac_f32_dpp %2, %4, %15 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
-      "v_fmac_f32_dpp %3, %4, %16 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
-      "v_fmac_f32_dpp %0, %4, %17 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
-      "v_fmac_f32_dpp %1, %4, %18 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
-      "v_fmac_f32_dpp %2, %4, %19 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
-      "v_fmac_f32_dpp %3, %4, %20 row_newbcast:15 row_mask:0xf bank_mask:0xf"
-      : "+v"(y0), "+v"(y1), "+v"(y2), "+v"(y3)
+      "v_fmac_f32_dpp %0, %2, %3 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %2, %4 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %2, %5 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %2, %6 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %2, %7 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %2, %8 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %2, %9 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %2, %10 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %2, %11 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %2, %12 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %2, %13 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %2, %14 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %2, %15 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %2, %16 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %2, %17 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %2, %18 row_newbcast:15 row_mask:0xf bank_mask:0xf"
+      : "+v"(y0), "+v"(y1)
       : "v"(c), "v"(h[0]), "v"(h[1]), "v"(h[2]), "v"(h[3]), "v"(h[4]), "v"(h[5]), "v"(h[6]), "v"(h[7]),
         "v"(h[8]), "v"(h[9]), "v"(h[10]), "v"(h[11]), "v"(h[12]), "v"(h[13]), "v"(h[14]), "v"(h[15]));
 }
@@ -201,19 +215,34 @@ struct Unroll<K, K> {
 
 // ---- the kernel ----------------------------------------------------------
 
+// dstate 16 fits 128 VGPRs, so two 8-wave workgroups share a CU (4 waves per
+// SIMD); wider states keep 2 waves per SIMD rather than spill.
+template <int G>
+constexpr int kMinWavesPerSimd = (G == 1) ? 4 : 2;
+
 template <typename IO, int G, int K, int W, bool SOFTPLUS, bool CLAMP>
-__global__ __launch_bounds__(64 * W) void ssm_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(64 * W, kMinWavesPerSimd<G>) void ssm_fwd_kernel(FwdParams p) {
   constexpr int N = 16 * G;             // states per channel
   constexpr int QR = 4 / G;             // time sub-chunks per wave
   constexpr int SUB = W * QR;           // sub-chunks per tile
   constexpr int T = SUB * K;            // steps per tile
-  constexpr int NS = N + 4;             // padded LDS row (channel) stride in floats
+  constexpr int NS = N + 4;             // padded row stride of the A table in floats
+  constexpr int AGG = SUB * 16 * N;     // floats of one tile's sub-chunk records
   constexpr int PAIRS = 16 * N;         // (channel, state) pairs of the workgroup
   constexpr int NT = 64 * W;            // threads
   constexpr int PPL = (PAIRS + NT - 1) / NT;
+  constexpr int E = Elem<IO>::kBytes;
 
-  __shared__ float agg_a[SUB * 16 * NS];
-  __shared__ float agg_b[SUB * 16 * NS];  // b_total, then overwritten with the incoming state
+  // Per tile and sub-chunk j, channel c, state n: b_total, then overwritten by
+  // the walk with the incoming state.  Stored as float4 quads,
+  // index ((j * N/4 + n/4) * 16 + c) * 4 + n%4, so that a row of 16 lanes
+  // writing one quad each, and a walk wave reading 16 channels x 4 states,
+  // both touch 64 consecutive dwords (no bank conflicts).  Two buffers
+  // alternate between tiles, so the next tile's pass 1 may write while the
+  // previous one is still being read.
+  __shared__ float agg_b[2][AGG];
+  __shared__ float agg_sd[2][SUB * 16];   // sum of delta over each sub-chunk, per channel
+  __shared__ float a2s[16 * NS];          // A * log2(e) for the workgroup's channels
 
   // Workgroup -> (batch row, channel group).  Workgroups are dealt to the 8
   // XCDs round-robin; consecutive logical ids are kept on one XCD so that
@@ -244,86 +273,126 @@ __global__ __launch_bounds__(64 * W) void ssm_fwd_kernel(FwdParams p) {
     len = v < 0 ? 0 : (v > L ? L : v);
   }
 
-  float A2[16];
-#pragma unroll
-  for (int s = 0; s < 16; ++s) A2[s] = -expf(p.A_log[static_cast<int64_t>(d) * N + 16 * g + s]) * kLog2e;
-  const float dskip = (p.D != nullptr) ? p.D[d] : 0.0f;
+  for (int k = tid; k < 16 * N; k += NT) {
+    const int cc = k / N, n = k % N;
+    a2s[cc * NS + n] = -expf(p.A_log[static_cast<int64_t>(cg * 16 + cc) * N + n]) * kLog2e;
+  }
+  // D*x is added once per (t, d): by the first state-group row only.
+  const float dskip = (p.D != nullptr && g == 0) ? p.D[d] : 0.0f;
 
   float carry[PPL];
 #pragma unroll
   for (int k = 0; k < PPL; ++k) carry[k] = 0.0f;
 
-  const int64_t row_xd = static_cast<int64_t>(b) * L * nd + d;          // x/delta/y index at t = 0
-  const int64_t row_bc = static_cast<int64_t>(b) * L * N + 16 * g + c;  // B/C index at t = 0 (lane holds state 16g+c)
-  const int64_t ntiles = (L + T - 1) / T;
-  const int64_t ntiles_valid = (len + T - 1) / T;
+  // Buffer resources of this batch row's x, delta, y, B and C, and the lane's
+  // byte offsets of its first step in a tile.
+  const int64_t xd_step = static_cast<int64_t>(nd) * E;  // bytes between consecutive steps of x/delta/y
+  const int64_t bc_step = static_cast<int64_t>(N) * E;   // ... of B/C
+  const int64_t xd_row = L * xd_step, bc_row = L * bc_step;
+  const rsrc_t rx = make_rsrc(static_cast<const char*>(p.x) + b * xd_row, xd_row);
+  const rsrc_t rd = make_rsrc(static_cast<const char*>(p.delta) + b * xd_row, xd_row);
+  const rsrc_t ry = make_rsrc(static_cast<char*>(p.y) + b * xd_row, xd_row);
+  const rsrc_t rb = make_rsrc(static_cast<const char*>(p.B) + b * bc_row, bc_row);
+  const rsrc_t rc = make_rsrc(static_cast<const char*>(p.C) + b * bc_row, bc_row);
+  const uint32_t off_xd = static_cast<uint32_t>((j * K * nd + d) * E);
+  const uint32_t off_bc = static_cast<uint32_t>((j * K * N + 16 * g + c) * E);
 
-  // One tile of T steps.  FULL: every step of the tile is valid (t < len).
-  auto tile_body = [&]<bool FULL>(int64_t tile) {
-    const int64_t t0 = tile * T + static_cast<int64_t>(j) * K;
-
-    float xv[K], dv[K], bv[K], cv[K];
+  // x and delta of the lane's K steps in the tile starting at t_tile.  Steps
+  // at or beyond len read as 0 (never loaded).
+  auto load_xd = [&]<bool FULL>(int64_t t_tile, float (&xv)[K], float (&dv)[K]) {
+    const int64_t left = len - t_tile - j * K;
 #pragma unroll
     for (int i = 0; i < K; ++i) {
-      const int64_t t = t0 + i;
-      const bool ok = FULL || t < len;
-      xv[i] = ok ? Elem<IO>::load(p.x, row_xd + t * nd) : 0.0f;
-      dv[i] = ok ? Elem<IO>::load(p.delta, row_xd + t * nd) : 0.0f;
-      bv[i] = ok ? Elem<IO>::load_cached(p.B, row_bc + t * N) : 0.0f;
-      cv[i] = ok ? Elem<IO>::load_cached(p.C, row_bc + t * N) : 0.0f;
+      const bool ok = FULL || i < left;
+      const uint32_t sx = static_cast<uint32_t>((t_tile + i) * xd_step);
+      xv[i] = ok ? Elem<IO>::template load<kStream>(rx, off_xd, sx) : 0.0f;
+      dv[i] = ok ? Elem<IO>::template load<kStream>(rd, off_xd, sx) : 0.0f;
+    }
+  };
+
+  // One tile of T steps starting at step t_tile, with its x and delta already
+  // in xv/dv.  FULL: every step of the tile is valid; otherwise steps at or
+  // beyond len are the identity and y there is +0.  When `prefetch` is set,
+  // the next tile's x and delta are requested into nxv/ndv before the work
+  // of this tile starts, so their latency hides behind it.
+  auto tile_body = [&]<bool FULL>(int64_t t_tile, int buf, float (&xv)[K], float (&dv)[K], bool prefetch,
+                                  float (&nxv)[K], float (&ndv)[K]) {
+    const int64_t left = len - t_tile - j * K;  // valid steps from this lane's first step
+    float bv[K], cv[K];
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      const bool ok = FULL || i < left;
+      const uint32_t sb = static_cast<uint32_t>((t_tile + i) * bc_step);
+      bv[i] = ok ? Elem<IO>::template load<0>(rb, off_bc, sb) : 0.0f;
+      cv[i] = ok ? Elem<IO>::template load<0>(rc, off_bc, sb) : 0.0f;
+    }
+    if (prefetch) load_xd.template operator()<true>(t_tile + T, nxv, ndv);
+    float A2[16];
+    {
+      const float* pa = a2s + c * NS + 16 * g;
+#pragma unroll
+      for (int s = 0; s < 16; s += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(pa + s);
+        A2[s] = v.x;
+        A2[s + 1] = v.y;
+        A2[s + 2] = v.z;
+        A2[s + 3] = v.w;
+      }
     }
 
     // ---- pass 1: discretise, cache Abar, fold the sub-chunk ----
     float ab[K][16];
     float u[K];
     float bt[16];
-#pragma unroll
-    for (int s = 0; s < 16; ++s) bt[s] = 0.0f;
     float sd = 0.0f;
+    float dls[K];
 #pragma unroll
-    for (int i = 0; i < K; ++i) {
+    for (int i = 0; i < K; ++i) {  // delta for all K steps first: covers the B/C load latency
       float dl = dv[i];
       if constexpr (SOFTPLUS) dl = softplus_f32(dl);
       if constexpr (CLAMP) dl = __builtin_amdgcn_fmed3f(dl, p.dmin, p.dmax);
-      if constexpr (!FULL) dl = (t0 + i < len) ? dl : 0.0f;  // padded step: delta = 0 -> Abar = 1
+      if constexpr (!FULL) dl = (i < left) ? dl : 0.0f;  // padded step: delta = 0 -> Abar = 1
+      dls[i] = dl;
       u[i] = dl * xv[i];
       sd += dl;
+    }
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      const float dl = dls[i];
       const float bi = bv[i];
       const float ui = u[i];
       Unroll<0, 16>::run([&]<int S>() {
         ab[i][S] = fast_exp2(dl * A2[S]);
-        bt[S] = __builtin_fmaf(ab[i][S], bt[S], row_bcast<S>(bi) * ui);
+        // the fold starts from zero: the first step's b_total is its b
+        bt[S] = (i == 0) ? row_bcast<S>(bi) * ui : __builtin_fmaf(ab[i][S], bt[S], row_bcast<S>(bi) * ui);
       });
     }
 
-    __syncthreads();  // the previous tile's pass 2 has read its incoming states
     {
-      float* pa = agg_a + (j * 16 + c) * NS + 16 * g;
-      float* pb = agg_b + (j * 16 + c) * NS + 16 * g;
+      float* pb = agg_b[buf] + ((j * (N / 4) + 4 * g) * 16 + c) * 4;
 #pragma unroll
-      for (int s = 0; s < 16; s += 4) {
-        *reinterpret_cast<float4*>(pa + s) =
-            make_float4(fast_exp2(A2[s] * sd), fast_exp2(A2[s + 1] * sd), fast_exp2(A2[s + 2] * sd),
-                        fast_exp2(A2[s + 3] * sd));
-        *reinterpret_cast<float4*>(pb + s) = make_float4(bt[s], bt[s + 1], bt[s + 2], bt[s + 3]);
-      }
+      for (int s = 0; s < 16; s += 4)
+        *reinterpret_cast<float4*>(pb + s * 16) = make_float4(bt[s], bt[s + 1], bt[s + 2], bt[s + 3]);
+      if (g == 0) agg_sd[buf][j * 16 + c] = sd;
     }
     __syncthreads();
 
     // ---- carry walk over the tile's sub-chunks, in time order ----
+    // The sub-chunk's decay is a_prod = prod_i exp(delta_i A) = exp2(A log2(e) sum_i delta_i).
 #pragma unroll
     for (int k = 0; k < PPL; ++k) {
       const int pr = tid + k * NT;
       if (PAIRS % NT == 0 || pr < PAIRS) {
-        const int cc = pr / N;
-        const int n = pr % N;
+        const int cc = pr % 16;  // walk lane -> (channel, state), channel fastest
+        const int n = pr / 16;
+        const float a2 = a2s[cc * NS + n];
         float cr = carry[k];
-#pragma unroll 4
+        float* pbw = agg_b[buf] + ((n / 4) * 16 + cc) * 4 + (n % 4);
+#pragma unroll 8
         for (int jj = 0; jj < SUB; ++jj) {
-          const int idx = (jj * 16 + cc) * NS + n;
-          const float a = agg_a[idx];
-          const float bb = agg_b[idx];
-          agg_b[idx] = cr;
+          const float a = fast_exp2(a2 * agg_sd[buf][jj * 16 + cc]);
+          const float bb = pbw[jj * (N / 4) * 64];
+          pbw[jj * (N / 4) * 64] = cr;
           cr = __builtin_fmaf(a, cr, bb);
         }
         carry[k] = cr;
@@ -334,10 +403,10 @@ __global__ __launch_bounds__(64 * W) void ssm_fwd_kernel(FwdParams p) {
     // ---- pass 2: states from the incoming state, readout ----
     float h[16];
     {
-      const float* pb = agg_b + (j * 16 + c) * NS + 16 * g;
+      const float* pb = agg_b[buf] + ((j * (N / 4) + 4 * g) * 16 + c) * 4;
 #pragma unroll
       for (int s = 0; s < 16; s += 4) {
-        const float4 v = *reinterpret_cast<const float4*>(pb + s);
+        const float4 v = *reinterpret_cast<const float4*>(pb + s * 16);
         h[s] = v.x;
         h[s + 1] = v.y;
         h[s + 2] = v.z;
@@ -351,34 +420,46 @@ __global__ __launch_bounds__(64 * W) void ssm_fwd_kernel(FwdParams p) {
       float bi = bv[i];
       asm volatile("" : "+v"(bi));
       const float ui = u[i];
-      float y0 = 0.0f, y1 = 0.0f, y2 = 0.0f, y3 = 0.0f;
+      float y0 = dskip * xv[i], y1 = 0.0f;
       Unroll<0, 16>::run([&]<int S>() { h[S] = __builtin_fmaf(ab[i][S], h[S], row_bcast<S>(bi) * ui); });
-      dot16_row_bcast(y0, y1, y2, y3, cv[i], h);
-      float yv = sum_state_groups<G>((y0 + y1) + (y2 + y3));
-      yv = __builtin_fmaf(dskip, xv[i], yv);
-      const int64_t t = t0 + i;
+      dot16_row_bcast(y0, y1, cv[i], h);
+      const float yv0 = sum_state_groups<G>(y0 + y1);
+      const uint32_t sx = static_cast<uint32_t>((t_tile + i) * xd_step);
       if constexpr (FULL) {
-        if (G == 1 || (i % G) == g) Elem<IO>::store(p.y, row_xd + t * nd, yv);
+        if (G == 1 || (i % G) == g) Elem<IO>::store(ry, off_xd, sx, yv0);
       } else {
-        if (t >= len) yv = 0.0f;
-        if (t < L && (G == 1 || (i % G) == g)) Elem<IO>::store(p.y, row_xd + t * nd, yv);
+        // the tile may run past L; only steps before L exist in y
+        const float yv = (i < left) ? yv0 : 0.0f;
+        if (i < L - t_tile - j * K && (G == 1 || (i % G) == g)) Elem<IO>::store(ry, off_xd, sx, yv);
       }
     }
   };
 
-  for (int64_t tile = 0; tile < ntiles; ++tile) {
-    if (tile >= ntiles_valid) {
-      // Whole tile is padding: the carry is unchanged and y is +0.
-      const int64_t t0 = tile * T + static_cast<int64_t>(j) * K;
+  __syncthreads();  // a2s is written
+  const int64_t nfull = len / T;
+  float xa[K], da[K], xn[K], dn[K];
+  if (nfull > 0) load_xd.template operator()<true>(0, xa, da);
+  for (int64_t tile = 0; tile < nfull; ++tile) {
+    tile_body.template operator()<true>(tile * T, static_cast<int>(tile & 1), xa, da, tile + 1 < nfull, xn, dn);
 #pragma unroll
-      for (int i = 0; i < K; ++i) {
-        const int64_t t = t0 + i;
-        if (t < L && (G == 1 || (i % G) == g)) Elem<IO>::store(p.y, row_xd + t * nd, 0.0f);
-      }
-    } else if ((tile + 1) * T <= len) {
-      tile_body.template operator()<true>(tile);
-    } else {
-      tile_body.template operator()<false>(tile);
+    for (int i = 0; i < K; ++i) {
+      xa[i] = xn[i];
+      da[i] = dn[i];
+    }
+  }
+  int64_t t_next = nfull * T;
+  if (t_next < len) {
+    load_xd.template operator()<false>(t_next, xa, da);
+    tile_body.template operator()<false>(t_next, static_cast<int>(nfull & 1), xa, da, false, xn, dn);
+    t_next += T;
+  }
+  // Tiles wholly in the padding: the carry is unchanged and y is +0.
+  for (; t_next < L; t_next += T) {
+    const int64_t left = L - t_next - j * K;
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      if (i < left && (G == 1 || (i % G) == g))
+        Elem<IO>::store(ry, off_xd, static_cast<uint32_t>((t_next + i) * xd_step), 0.0f);
     }
   }
 
@@ -387,8 +468,8 @@ __global__ __launch_bounds__(64 * W) void ssm_fwd_kernel(FwdParams p) {
     for (int k = 0; k < PPL; ++k) {
       const int pr = tid + k * NT;
       if (PAIRS % NT == 0 || pr < PAIRS) {
-        const int cc = pr / N;
-        const int n = pr % N;
+        const int cc = pr % 16;
+        const int n = pr / 16;
         p.h_last[(static_cast<int64_t>(b) * nd + cg * 16 + cc) * N + n] = carry[k];
       }
     }
@@ -536,8 +617,10 @@ int ssm_selective_scan_fwd(ssm_scan_t handle, const void* x, const void* delta, 
   // indices are 64-bit in the kernel.
   if (nb > 0 && nd > 0 && (nb * (nd / 16) > 0x7fffffffLL || nb > 0x7fffffffLL || nd > 0x7fffffffLL))
     return SSM_ERR_UNSUPPORTED;
-  if (L > 0 && nb > 0 && nd > 0 && L > (int64_t{1} << 62) / (nb * nd * (N > nd ? N : nd)))
-    return SSM_ERR_UNSUPPORTED;
+  // A batch row of x, delta, y, B or C must span fewer than 2^31 bytes (it is
+  // addressed through one buffer resource with 32-bit offsets).
+  const int64_t esz = dims->io_dtype == SSM_IO_BF16 ? 2 : 4;
+  if (L > 0 && L * (N > nd ? N : nd) * esz > 0x7fffffffLL) return SSM_ERR_UNSUPPORTED;
 
   const bool empty = (nb == 0 || nd == 0);
   const size_t e = dims->io_dtype == SSM_IO_BF16 ? 2 : 4;
