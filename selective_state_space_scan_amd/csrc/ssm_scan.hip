@@ -240,9 +240,9 @@ __global__ __launch_bounds__(64 * W, kMinWavesPerSimd<G>) void ssm_fwd_kernel(Fw
   // both touch 64 consecutive dwords (no bank conflicts).  Two buffers
   // alternate between tiles, so the next tile's pass 1 may write while the
   // previous one is still being read.
-  __shared__ float agg_b[2][AGG];
+  __shared__ __attribute__((aligned(16))) float agg_b[2][AGG];
   __shared__ float agg_sd[2][SUB * 16];   // sum of delta over each sub-chunk, per channel
-  __shared__ float a2s[16 * NS];          // A * log2(e) for the workgroup's channels
+  __shared__ __attribute__((aligned(16))) float a2s[16 * NS];  // A * log2(e) for the workgroup's channels
 
   // Workgroup -> (batch row, channel group).  Workgroups are dealt to the 8
   // XCDs round-robin; consecutive logical ids are kept on one XCD so that
