@@ -62,11 +62,15 @@ def _load(mutation: int = 0) -> ctypes.CDLL:
         lib.oracle_scan_ab.restype = None
         lib.oracle_softplus.argtypes = [ctypes.c_double]
         lib.oracle_softplus.restype = ctypes.c_double
+        lib.oracle_silu.argtypes = [ctypes.c_double]
+        lib.oracle_silu.restype = ctypes.c_double
         common = [d, d, d, d, d, d, i32, d, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int,
                   ctypes.c_double, ctypes.c_double]
         lib.oracle_selective_scan.argtypes = common + [d, d, ctypes.c_int]
         lib.oracle_selective_scan.restype = ctypes.c_int
-        lib.oracle_selective_scan_rows.argtypes = common + [i64p, i64p, i64, d, d, ctypes.c_int]
+        lib.oracle_selective_scan_ex.argtypes = common + [d, d, d, i64, d, d, ctypes.c_int]
+        lib.oracle_selective_scan_ex.restype = ctypes.c_int
+        lib.oracle_selective_scan_rows.argtypes = common + [d, d, i64p, i64p, i64, d, d, ctypes.c_int]
         lib.oracle_selective_scan_rows.restype = ctypes.c_int
         lib.oracle_mutation_id.argtypes = []
         lib.oracle_mutation_id.restype = ctypes.c_int
@@ -101,6 +105,10 @@ def softplus(v: float, mutation: int = 0) -> float:
     return _load(mutation).oracle_softplus(float(v))
 
 
+def silu(v: float, mutation: int = 0) -> float:
+    return _load(mutation).oracle_silu(float(v))
+
+
 def _prep(x, delta, A_log, B, C, D, valid_len, h0):
     x = _f64(x)
     delta = _f64(delta)
@@ -129,26 +137,46 @@ def _prep(x, delta, A_log, B, C, D, valid_len, h0):
     return x, delta, A_log, B, C, D, vl, h0, nb, L, nd, N
 
 
+def _extras(delta_bias, z, nb, L, nd):
+    delta_bias = _f64(delta_bias)
+    z = _f64(z)
+    if delta_bias is not None and delta_bias.shape != (nd,):
+        raise ValueError("delta_bias must be [D]")
+    if z is not None and z.shape != (nb, L, nd):
+        raise ValueError("z must be [B, L, D]")
+    return delta_bias, z
+
+
 def selective_scan(x, delta, A_log, B, C, D=None, valid_len=None, h0=None, delta_softplus: bool = True,
-                   delta_clamp=None, nthreads: int = 1, mutation: int = 0):
-    """Full forward.  Returns (y [B,L,D], h_last [B,D,N]) in fp64."""
+                   delta_clamp=None, delta_bias=None, z=None, chunk_len=None, nthreads: int = 1, mutation: int = 0):
+    """Full forward.  Returns (y [B,L,D], h_last [B,D,N]) in fp64, and with
+    ``chunk_len`` also the chunk-boundary states [B, ceil(L/chunk_len), D, N]."""
     x, delta, A_log, B, C, D, vl, h0, nb, L, nd, N = _prep(x, delta, A_log, B, C, D, valid_len, h0)
+    delta_bias, z = _extras(delta_bias, z, nb, L, nd)
     clamp = delta_clamp is not None
     dmin, dmax = (float(delta_clamp[0]), float(delta_clamp[1])) if clamp else (0.0, 0.0)
     y = np.empty((nb, L, nd), dtype=np.float64)
     h_last = np.empty((nb, nd, N), dtype=np.float64)
-    rc = _load(mutation).oracle_selective_scan(
+    cs = None
+    if chunk_len is not None:
+        cs = np.empty((nb, (L + chunk_len - 1) // chunk_len, nd, N), dtype=np.float64)
+    rc = _load(mutation).oracle_selective_scan_ex(
         _ptr(x), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(vl, ctypes.c_int32), _ptr(h0),
-        nb, L, nd, N, int(bool(delta_softplus)), int(clamp), dmin, dmax, _ptr(y), _ptr(h_last), int(nthreads))
+        nb, L, nd, N, int(bool(delta_softplus)), int(clamp), dmin, dmax, _ptr(delta_bias), _ptr(z), _ptr(cs),
+        int(chunk_len or 1), _ptr(y), _ptr(h_last), int(nthreads))
     if rc != 0:
         raise RuntimeError(f"oracle_selective_scan failed ({rc})")
+    if chunk_len is not None:
+        return y, h_last, cs
     return y, h_last
 
 
 def selective_scan_rows(x, delta, A_log, B, C, rows, D=None, valid_len=None, h0=None,
-                        delta_softplus: bool = True, delta_clamp=None, nthreads: int = 1, mutation: int = 0):
+                        delta_softplus: bool = True, delta_clamp=None, delta_bias=None, z=None, nthreads: int = 1,
+                        mutation: int = 0):
     """Forward for the listed (b, d) rows only.  Returns (y_rows [R, L], h_rows [R, N])."""
     x, delta, A_log, B, C, D, vl, h0, nb, L, nd, N = _prep(x, delta, A_log, B, C, D, valid_len, h0)
+    delta_bias, z = _extras(delta_bias, z, nb, L, nd)
     rows = np.asarray(rows, dtype=np.int64).reshape(-1, 2)
     rb = np.ascontiguousarray(rows[:, 0])
     rd = np.ascontiguousarray(rows[:, 1])
@@ -159,7 +187,8 @@ def selective_scan_rows(x, delta, A_log, B, C, rows, D=None, valid_len=None, h0=
     h = np.empty((R, N), dtype=np.float64)
     rc = _load(mutation).oracle_selective_scan_rows(
         _ptr(x), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(vl, ctypes.c_int32), _ptr(h0),
-        nb, L, nd, N, int(bool(delta_softplus)), int(clamp), dmin, dmax, _ptr(rb, ctypes.c_int64),
+        nb, L, nd, N, int(bool(delta_softplus)), int(clamp), dmin, dmax, _ptr(delta_bias), _ptr(z),
+        _ptr(rb, ctypes.c_int64),
         _ptr(rd, ctypes.c_int64), R, _ptr(y), _ptr(h), int(nthreads))
     if rc != 0:
         raise RuntimeError(f"oracle_selective_scan_rows failed ({rc})")

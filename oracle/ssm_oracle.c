@@ -23,6 +23,13 @@
  *    the last valid step.
  *  - Zero initial state unless h0 is given (pwwt.cn section 4.1, the naive
  *    reference loop starts from zeros when no h0 is passed).
+ *  - Optional extras of the fused kernel the nxbn.cn article describes
+ *    (section 3, its kernel body): a per-channel bias added to the raw delta
+ *    before softplus, and an output gate y <- y * silu(z), silu(z) =
+ *    z / (1 + e^-z), applied to the full readout (C.h + D x).  Optional
+ *    chunk-boundary states: the state after the last step of every chunk of
+ *    chunk_len steps (the boundary states of the pwwt.cn article, section 3.4,
+ *    kept for recomputation).
  *
  * Every input arrives as fp64 (bf16 and fp32 inputs convert exactly); all
  * arithmetic is fp64 with the C library's exp/log1p.
@@ -79,12 +86,19 @@ typedef struct {
   int64_t nb, L, nd, N;
   int softplus, clamp;
   double dmin, dmax;
+  const double* delta_bias; /* [nd] or NULL */
+  const double* z;          /* [nb, L, nd] or NULL */
+  double* chunk_states;     /* [nb, nchunks, nd, N] or NULL (full runs only) */
+  int64_t chunk_len;
 } problem_t;
+
+/* silu(v) = v * sigmoid(v) = v / (1 + e^-v). */
+ORACLE_API double oracle_silu(double v) { return v / (1.0 + exp(-v)); }
 
 /* One (b, d) row over all L steps.  y_out[t] for t in [0, L) with stride
  * y_stride; h_out[n] for n in [0, N). */
 static void scan_row(const problem_t* p, int64_t b, int64_t d, double* y_out, int64_t y_stride, double* h_out,
-                     double* h /* scratch, N */, double* A /* scratch, N */) {
+                     double* h /* scratch, N */, double* A /* scratch, N */, double* cs_out /* chunk states or NULL */) {
   const int64_t L = p->L, N = p->N, nd = p->nd;
   int64_t len = L;
   if (p->valid_len) {
@@ -106,13 +120,23 @@ static void scan_row(const problem_t* p, int64_t b, int64_t d, double* y_out, in
       for (int64_t n = 0; n < N; ++n) h[n] = 0.0; /* planted: padding resets the state */
 #endif
       y_out[t * y_stride] = 0.0;
+      if (cs_out && ((t + 1) % p->chunk_len == 0 || t == L - 1))
+        for (int64_t n = 0; n < N; ++n) cs_out[(t / p->chunk_len) * p->nd * N + n] = h[n];
       continue;
     }
     const int64_t i = (b * L + t) * nd + d;
     const double xt = p->x[i];
     double dt = p->delta[i];
+#if ORACLE_MUTATION == 10
 #if ORACLE_MUTATION != 5
     if (p->softplus) dt = oracle_softplus(dt);
+#endif
+    if (p->delta_bias) dt += p->delta_bias[d]; /* planted: bias added after softplus */
+#else
+    if (p->delta_bias) dt += p->delta_bias[d];
+#if ORACLE_MUTATION != 5
+    if (p->softplus) dt = oracle_softplus(dt);
+#endif
 #endif
     if (p->clamp) {
       if (dt < p->dmin) dt = p->dmin;
@@ -142,10 +166,18 @@ static void scan_row(const problem_t* p, int64_t b, int64_t d, double* y_out, in
 #endif
     }
 #if ORACLE_MUTATION == 4
-    y_out[t * y_stride] = acc; /* planted: skip term dropped */
+    double yt = acc; /* planted: skip term dropped */
 #else
-    y_out[t * y_stride] = acc + dskip * xt;
+    double yt = acc + dskip * xt;
 #endif
+#if ORACLE_MUTATION == 9
+    if (p->z) yt = acc * oracle_silu(p->z[i]) + dskip * xt; /* planted: gate before the skip term */
+#else
+    if (p->z) yt *= oracle_silu(p->z[i]);
+#endif
+    y_out[t * y_stride] = yt;
+    if (cs_out && ((t + 1) % p->chunk_len == 0 || t == L - 1))
+      for (int64_t n = 0; n < N; ++n) cs_out[(t / p->chunk_len) * p->nd * N + n] = h[n];
   }
   if (h_out)
     for (int64_t n = 0; n < N; ++n) h_out[n] = h[n];
@@ -194,7 +226,12 @@ static void* worker(void* argp) {
       ystride = p->nd;
       ho = j->h_last ? j->h_last + (b * p->nd + d) * p->N : NULL;
     }
-    scan_row(p, b, d, yo, ystride, ho, scratch, scratch + p->N);
+    double* cs = NULL;
+    if (!j->rb && p->chunk_states) {
+      const int64_t nch = (p->L + p->chunk_len - 1) / p->chunk_len;
+      cs = p->chunk_states + (b * nch * p->nd + d) * p->N;
+    }
+    scan_row(p, b, d, yo, ystride, ho, scratch, scratch + p->N, cs);
   }
   free(scratch);
   return NULL;
@@ -229,6 +266,31 @@ static int run_job(job_t* job, int nthreads) {
   return job->status;
 }
 
+/* Full forward with the optional extras: delta_bias [nd] (added to the raw
+ * delta before softplus), z [nb, L, nd] (output gate y * silu(z)), and
+ * chunk_states [nb, ceil(L / chunk_len), nd, N] (state after the last step of
+ * each chunk, the last chunk possibly shorter).  Any of them may be NULL. */
+ORACLE_API int oracle_selective_scan_ex(const double* x, const double* delta, const double* A_log, const double* B,
+                                        const double* C, const double* D, const int32_t* valid_len,
+                                        const double* h0, int64_t nb, int64_t L, int64_t nd, int64_t N, int softplus,
+                                        int clamp, double dmin, double dmax, const double* delta_bias,
+                                        const double* z, double* chunk_states, int64_t chunk_len, double* y,
+                                        double* h_last, int nthreads) {
+  if (nb < 0 || L < 0 || nd < 0 || N < 1 || !y) return -3;
+  if (L > 0 && (!x || !delta || !B || !C)) return -3;
+  if (!A_log) return -3;
+  if (chunk_states && chunk_len < 1) return -3;
+  problem_t p = {x, delta, A_log, B, C, D, h0, valid_len, nb, L, nd, N, softplus, clamp, dmin, dmax,
+                 delta_bias, z, chunk_states, chunk_len};
+  job_t job;
+  memset(&job, 0, sizeof(job));
+  job.p = &p;
+  job.nrows = nb * nd;
+  job.y = y;
+  job.h_last = h_last;
+  return run_job(&job, nthreads);
+}
+
 /* Full forward over every (b, d) row.  Layouts (row-major, contiguous):
  * x, delta, y: [nb, L, nd]; A_log: [nd, N]; B, C: [nb, L, N]; D: [nd] or NULL;
  * valid_len: [nb] or NULL (all L); h0: [nb, nd, N] or NULL (zeros);
@@ -241,7 +303,8 @@ ORACLE_API int oracle_selective_scan(const double* x, const double* delta, const
   if (nb < 0 || L < 0 || nd < 0 || N < 1 || !y) return -3;
   if (L > 0 && (!x || !delta || !B || !C)) return -3;
   if (!A_log) return -3;
-  problem_t p = {x, delta, A_log, B, C, D, h0, valid_len, nb, L, nd, N, softplus, clamp, dmin, dmax};
+  problem_t p = {x, delta, A_log, B, C, D, h0, valid_len, nb, L, nd, N, softplus, clamp, dmin, dmax,
+                 NULL, NULL, NULL, 1};
   job_t job;
   memset(&job, 0, sizeof(job));
   job.p = &p;
@@ -256,7 +319,8 @@ ORACLE_API int oracle_selective_scan(const double* x, const double* delta, const
 ORACLE_API int oracle_selective_scan_rows(const double* x, const double* delta, const double* A_log, const double* B,
                                           const double* C, const double* D, const int32_t* valid_len,
                                           const double* h0, int64_t nb, int64_t L, int64_t nd, int64_t N,
-                                          int softplus, int clamp, double dmin, double dmax, const int64_t* row_b,
+                                          int softplus, int clamp, double dmin, double dmax,
+                                          const double* delta_bias, const double* z, const int64_t* row_b,
                                           const int64_t* row_d, int64_t nrows, double* y_rows, double* h_rows,
                                           int nthreads) {
   if (nb < 0 || L < 0 || nd < 0 || N < 1 || !y_rows || nrows < 0 || !row_b || !row_d) return -3;
@@ -264,7 +328,8 @@ ORACLE_API int oracle_selective_scan_rows(const double* x, const double* delta, 
   if (!A_log) return -3;
   for (int64_t r = 0; r < nrows; ++r)
     if (row_b[r] < 0 || row_b[r] >= nb || row_d[r] < 0 || row_d[r] >= nd) return -3;
-  problem_t p = {x, delta, A_log, B, C, D, h0, valid_len, nb, L, nd, N, softplus, clamp, dmin, dmax};
+  problem_t p = {x, delta, A_log, B, C, D, h0, valid_len, nb, L, nd, N, softplus, clamp, dmin, dmax,
+                 delta_bias, z, NULL, 1};
   job_t job;
   memset(&job, 0, sizeof(job));
   job.p = &p;

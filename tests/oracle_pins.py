@@ -304,6 +304,57 @@ def pin_bruteforce_full(orc, mutation=0):
             assert np.max(np.abs(h[bi, d] - hs)) <= 1e-12 * max(1.0, np.max(np.abs(hs)))
 
 
+# ---- extras: delta bias, output gate, chunk-boundary states ----------------
+
+def pin_delta_bias(orc, mutation=0):
+    """The per-channel bias is added to the raw delta before softplus: a biased
+    run equals an unbiased run on delta + bias (bitwise: the same fp64 sum)."""
+    rng = np.random.default_rng(23)
+    nb, L, nd, N = 2, 20, 8, 4
+    x, delta, A_log, B, C, D = _rand_problem(rng, nb, L, nd, N)
+    bias = rng.standard_normal(nd)
+    y1, h1 = orc.selective_scan(x, delta, A_log, B, C, D, delta_bias=bias, mutation=mutation)
+    y2, h2 = orc.selective_scan(x, delta + bias[None, None, :], A_log, B, C, D, mutation=mutation)
+    assert np.array_equal(y1, y2) and np.array_equal(h1, h2)
+
+
+def pin_output_gate(orc, mutation=0):
+    """y <- y * silu(z) with silu(v) = v / (1 + e^-v), applied to the whole
+    readout C.h + D x (nxbn.cn section 3's kernel body ends with the gate): the
+    gated output is the ungated one times silu(z), z = 0 gives +-0, and the
+    state is untouched."""
+    rng = np.random.default_rng(29)
+    nb, L, nd, N = 2, 20, 8, 4
+    x, delta, A_log, B, C, D = _rand_problem(rng, nb, L, nd, N)
+    z = rng.standard_normal((nb, L, nd)) * 3.0
+    z[0, 3, :] = 0.0
+    yg, hg = orc.selective_scan(x, delta, A_log, B, C, D, z=z, mutation=mutation)
+    y, h = orc.selective_scan(x, delta, A_log, B, C, D, mutation=mutation)
+    silu = z / (1.0 + np.exp(-z))
+    assert np.max(np.abs(yg - y * silu) / np.maximum(np.abs(y * silu), 1e-300)) < 1e-14
+    assert np.all(yg[0, 3, :] == 0.0) and np.array_equal(h, hg)
+    assert orc.silu(0.0, mutation=mutation) == 0.0
+    assert abs(orc.silu(40.0, mutation=mutation) - 40.0) < 1e-12
+
+
+def pin_chunk_states(orc, mutation=0):
+    """The state after each chunk equals the final state of the same run cut
+    at the chunk's end (also with padded rows: past the valid length the state
+    no longer changes)."""
+    rng = np.random.default_rng(31)
+    nb, L, nd, N, cl = 3, 23, 8, 4, 5
+    x, delta, A_log, B, C, D = _rand_problem(rng, nb, L, nd, N)
+    vl = np.array([23, 12, 0], dtype=np.int32)
+    y, h, cs = orc.selective_scan(x, delta, A_log, B, C, D, valid_len=vl, chunk_len=cl, mutation=mutation)
+    assert cs.shape == (nb, 5, nd, N)
+    for k in range(cs.shape[1]):
+        end = min((k + 1) * cl, L)
+        _, hk = orc.selective_scan(x[:, :end], delta[:, :end], A_log, B[:, :end], C[:, :end], D,
+                                   valid_len=np.minimum(vl, end), mutation=mutation)
+        assert np.array_equal(cs[:, k], hk), k
+    assert np.array_equal(cs[:, -1], h)
+
+
 ALL_PINS = {
     "closed_form_scan": pin_closed_form_scan,
     "closed_form_full_path": pin_closed_form_full_path,
@@ -316,6 +367,9 @@ ALL_PINS = {
     "softplus": pin_softplus,
     "split_invariance": pin_split_invariance,
     "bruteforce_full": pin_bruteforce_full,
+    "delta_bias": pin_delta_bias,
+    "output_gate": pin_output_gate,
+    "chunk_states": pin_chunk_states,
 }
 
 # The planted mistakes (see ssm_oracle.c) and the pins expected to notice each.
@@ -328,4 +382,6 @@ MUTATIONS = {
     6: ("delta missing from the input term", {"lti_convolution", "bruteforce_full"}),
     7: ("padding resets the state", {"identity_and_padding"}),
     8: ("B and C swapped in the input term", {"bruteforce_full"}),
+    9: ("output gate applied before the skip term", {"output_gate"}),
+    10: ("delta bias added after softplus", {"delta_bias"}),
 }
