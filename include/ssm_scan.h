@@ -94,6 +94,46 @@ int ssm_selective_scan_fwd(ssm_scan_t handle, const void* x, const void* delta, 
                            const void* C, const float* D, const int32_t* valid_len, void* y, float* h_last,
                            const ssm_scan_dims* dims, void* stream);
 
+/* Optional inputs and outputs of the forward (any field may be NULL/0).
+ *
+ *  h0           [batch, dim, dstate] fp32: the state before step 0 instead of
+ *               zeros (continuing a sequence processed in pieces: the split
+ *               run equals the whole run, pwwt.cn section 4.2 and
+ *               bjdmk.com.cn section 2.4 carry the state between chunks).
+ *               h0 may be the same buffer as h_last (in-place update); any
+ *               other overlap with an output is rejected.
+ *  delta_bias   [dim] fp32: added to delta before softplus and the clip (the
+ *               dt bias of the fused kernel body in the nxbn.cn article,
+ *               section 3).
+ *  z            [batch, seqlen, dim], io dtype: output gate, y <- y * silu(z)
+ *               with silu(v) = v / (1 + e^-v), applied to the whole readout
+ *               C.h + D*x at valid steps (the same article and section).
+ *  chunk_states [batch, ceil(seqlen / chunk_len), dim, dstate] fp32: the state
+ *               after the last step of every chunk of chunk_len steps (the last
+ *               chunk may be shorter; past valid_len the state no longer
+ *               changes) -- the boundary states kept for recomputation in the
+ *               pwwt.cn article, section 3.4.
+ *  chunk_len    must equal ssm_scan_chunk_len(dstate) when chunk_states is set. */
+typedef struct ssm_scan_fwd_extras {
+  const float* h0;
+  const float* delta_bias;
+  const void* z;
+  float* chunk_states;
+  int64_t chunk_len;
+} ssm_scan_fwd_extras;
+
+/* Steps per chunk of chunk_states for this dstate (the kernel's time tile):
+ * 128, 64 or 32 for dstate 16, 32 or 64; 0 for an unsupported dstate. */
+int64_t ssm_scan_chunk_len(int64_t dstate);
+
+/* ssm_selective_scan_fwd with the optional extras above (extras may be NULL,
+ * which is ssm_selective_scan_fwd).  Same ordering, asynchrony and errors;
+ * additionally SSM_ERR_INVALID_ARG for a chunk_len that does not match, and
+ * SSM_ERR_ALIAS for an extra output overlapping an input or another output. */
+int ssm_selective_scan_fwd_ex(ssm_scan_t handle, const void* x, const void* delta, const float* A_log, const void* B,
+                              const void* C, const float* D, const int32_t* valid_len, void* y, float* h_last,
+                              const ssm_scan_dims* dims, const ssm_scan_fwd_extras* extras, void* stream);
+
 /* Release the handle.  NULL is accepted.  The caller must ensure no work
  * enqueued with the handle is still to be launched. */
 int ssm_scan_destroy(ssm_scan_t handle);

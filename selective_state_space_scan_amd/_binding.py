@@ -25,7 +25,8 @@ SSM_IO_F32 = 0
 SSM_IO_BF16 = 1
 
 # Names declared in include/ssm_scan.h.
-EXPORTED = ("ssm_scan_create", "ssm_selective_scan_fwd", "ssm_scan_destroy", "ssm_scan_error_string")
+EXPORTED = ("ssm_scan_create", "ssm_selective_scan_fwd", "ssm_selective_scan_fwd_ex", "ssm_scan_chunk_len",
+            "ssm_scan_destroy", "ssm_scan_error_string")
 
 
 class SsmScanError(RuntimeError):
@@ -45,6 +46,16 @@ class ssm_scan_dims(ctypes.Structure):
         ("delta_clamp", ctypes.c_int32),
         ("delta_min", ctypes.c_float),
         ("delta_max", ctypes.c_float),
+    ]
+
+
+class ssm_scan_fwd_extras(ctypes.Structure):
+    _fields_ = [
+        ("h0", ctypes.c_void_p),
+        ("delta_bias", ctypes.c_void_p),
+        ("z", ctypes.c_void_p),
+        ("chunk_states", ctypes.c_void_p),
+        ("chunk_len", ctypes.c_int64),
     ]
 
 
@@ -77,6 +88,11 @@ def lib() -> ctypes.CDLL:
         L.ssm_selective_scan_fwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                              ctypes.POINTER(ssm_scan_dims), vp]
         L.ssm_selective_scan_fwd.restype = ctypes.c_int
+        L.ssm_selective_scan_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                ctypes.POINTER(ssm_scan_dims), ctypes.POINTER(ssm_scan_fwd_extras), vp]
+        L.ssm_selective_scan_fwd_ex.restype = ctypes.c_int
+        L.ssm_scan_chunk_len.argtypes = [ctypes.c_int64]
+        L.ssm_scan_chunk_len.restype = ctypes.c_int64
         _lib = L
         return L
 
@@ -108,6 +124,19 @@ def ssm_selective_scan_fwd(handle, x, delta, A_log, B, C, D, valid_len, y, h_las
                                         ctypes.byref(dims), stream)
 
 
+def ssm_selective_scan_fwd_ex(handle, x, delta, A_log, B, C, D, valid_len, y, h_last, dims: ssm_scan_dims,
+                              extras: ssm_scan_fwd_extras | None, stream) -> int:
+    """The extended entry point (raw pointers); returns the status code."""
+    return lib().ssm_selective_scan_fwd_ex(handle, x, delta, A_log, B, C, D, valid_len, y, h_last,
+                                           ctypes.byref(dims), None if extras is None else ctypes.byref(extras),
+                                           stream)
+
+
+def chunk_len(dstate: int) -> int:
+    """Steps per chunk of the chunk-boundary states for this state count."""
+    return int(lib().ssm_scan_chunk_len(int(dstate)))
+
+
 # ---- torch front end -----------------------------------------------------
 
 _handles: dict[int, int] = {}
@@ -124,8 +153,10 @@ def handle_for(device_index: int) -> int:
 
 
 def selective_scan_fwd(x, delta, A_log, B, C, D=None, valid_len=None, *, delta_softplus: bool = True,
-                       delta_clamp=None, y=None, h_last=None, return_h_last: bool = True, stream=None):
-    """Selective-scan forward on the GPU.  Returns ``(y, h_last)``.
+                       delta_clamp=None, y=None, h_last=None, return_h_last: bool = True, h0=None, delta_bias=None,
+                       z=None, return_chunk_states: bool = False, stream=None):
+    """Selective-scan forward on the GPU.  Returns ``(y, h_last)``, or
+    ``(y, h_last, chunk_states)`` with ``return_chunk_states``.
 
     x, delta: [batch, L, dim]; B, C: [batch, L, dstate]; all four the same dtype
     (torch.float32 or torch.bfloat16).  A_log: [dim, dstate] float32.  D: [dim]
@@ -134,6 +165,11 @@ def selective_scan_fwd(x, delta, A_log, B, C, D=None, valid_len=None, *, delta_s
     y like x, h_last [batch, dim, dstate] float32 (None if return_h_last is
     False and no h_last is given).  The call is asynchronous on ``stream``
     (default: the current stream of x's device).
+
+    Extras: h0 [batch, dim, dstate] float32 initial state (may be h_last
+    itself); delta_bias [dim] float32 added to delta before softplus; z like x,
+    output gate y * silu(z); chunk states [batch, ceil(L / chunk_len(dstate)),
+    dim, dstate] float32, the state after every chunk.
     """
     import torch
 
@@ -173,6 +209,17 @@ def selective_scan_fwd(x, delta, A_log, B, C, D=None, valid_len=None, *, delta_s
                                  or h_last.device != dev or not h_last.is_contiguous()):
         raise ValueError("h_last must be a contiguous [batch, dim, dstate] float32 tensor")
 
+    for name, t, shape in (("h0", h0, (nb, nd, N)), ("delta_bias", delta_bias, (nd,))):
+        if t is not None and (tuple(t.shape) != shape or t.dtype != torch.float32 or t.device != dev
+                              or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous {shape} float32 tensor on x's device")
+    if z is not None and (tuple(z.shape) != (nb, L, nd) or z.dtype != x.dtype or z.device != dev
+                          or not z.is_contiguous()):
+        raise ValueError("z must be a contiguous tensor like x")
+    cl = chunk_len(N)
+    chunk_states = None
+    if return_chunk_states:
+        chunk_states = torch.empty((nb, (L + cl - 1) // cl, nd, N), dtype=torch.float32, device=dev)
     dims = ssm_scan_dims()
     dims.batch, dims.seqlen, dims.dim, dims.dstate = nb, L, nd, N
     dims.io_dtype = io
@@ -187,10 +234,20 @@ def selective_scan_fwd(x, delta, A_log, B, C, D=None, valid_len=None, *, delta_s
     def ptr(t):
         return None if t is None or t.numel() == 0 else t.data_ptr()
 
+    extras = None
+    if h0 is not None or delta_bias is not None or z is not None or chunk_states is not None:
+        extras = ssm_scan_fwd_extras(ptr(h0), ptr(delta_bias), ptr(z), ptr(chunk_states),
+                                     cl if chunk_states is not None else 0)
     with torch.cuda.device(dev):
         h = handle_for(dev.index if dev.index is not None else torch.cuda.current_device())
-        rc = ssm_selective_scan_fwd(h, ptr(x), ptr(delta), ptr(A_log), ptr(B), ptr(C), ptr(D), ptr(valid_len),
-                                    ptr(y), ptr(h_last), dims, sptr)
+        if extras is None:
+            rc = ssm_selective_scan_fwd(h, ptr(x), ptr(delta), ptr(A_log), ptr(B), ptr(C), ptr(D), ptr(valid_len),
+                                        ptr(y), ptr(h_last), dims, sptr)
+        else:
+            rc = ssm_selective_scan_fwd_ex(h, ptr(x), ptr(delta), ptr(A_log), ptr(B), ptr(C), ptr(D),
+                                           ptr(valid_len), ptr(y), ptr(h_last), dims, extras, sptr)
     if rc != SSM_OK:
         raise SsmScanError(rc, "ssm_selective_scan_fwd")
+    if return_chunk_states:
+        return y, h_last, chunk_states
     return y, h_last

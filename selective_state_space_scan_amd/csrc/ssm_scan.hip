@@ -61,6 +61,10 @@ struct FwdParams {
   const int32_t* valid_len;
   void* y;
   float* h_last;
+  const float* h0;
+  const float* delta_bias;
+  const void* z;
+  float* chunk_states;
   int64_t L;
   int32_t nb;
   int32_t nd;
@@ -220,7 +224,7 @@ struct Unroll<K, K> {
 template <int G>
 constexpr int kMinWavesPerSimd = (G == 1) ? 4 : 2;
 
-template <typename IO, int G, int K, int W, bool SOFTPLUS, bool CLAMP>
+template <typename IO, int G, int K, int W, bool SOFTPLUS, bool CLAMP, bool GATE>
 __global__ __launch_bounds__(64 * W, kMinWavesPerSimd<G>) void ssm_fwd_kernel(FwdParams p) {
   constexpr int N = 16 * G;             // states per channel
   constexpr int QR = 4 / G;             // time sub-chunks per wave
@@ -279,10 +283,42 @@ __global__ __launch_bounds__(64 * W, kMinWavesPerSimd<G>) void ssm_fwd_kernel(Fw
   }
   // D*x is added once per (t, d): by the first state-group row only.
   const float dskip = (p.D != nullptr && g == 0) ? p.D[d] : 0.0f;
+  const float dbias = (p.delta_bias != nullptr) ? p.delta_bias[d] : 0.0f;
+
+  // The walk lane's (channel, state) pair k: channel fastest.
+  auto pair_of = [&](int k, int& cc, int& n) {
+    const int pr = tid + k * NT;
+    cc = pr % 16;
+    n = pr / 16;
+  };
+  auto pair_valid = [&](int k) { return PAIRS % NT == 0 || tid + k * NT < PAIRS; };
+  // Offset of pair k within the workgroup's 16 x N block of a [.., dim, dstate]
+  // tensor (the block itself starts at a wave-uniform address).
+  auto pair_offset = [&](int k) {
+    int cc, n;
+    pair_of(k, cc, n);
+    return static_cast<uint32_t>(cc * N + n);
+  };
+  const int64_t state_block = (static_cast<int64_t>(b) * nd + cg * 16) * N;
 
   float carry[PPL];
 #pragma unroll
   for (int k = 0; k < PPL; ++k) carry[k] = 0.0f;
+  if (p.h0 != nullptr) {
+    const float* h0b = p.h0 + state_block;
+#pragma unroll
+    for (int k = 0; k < PPL; ++k)
+      if (pair_valid(k)) carry[k] = h0b[pair_offset(k)];
+  }
+  // Chunk-boundary states: the carry after each tile.
+  const int64_t n_chunks = (L + T - 1) / T;
+  auto store_chunk_state = [&](int64_t tile) {
+    if (p.chunk_states == nullptr) return;
+    float* cb = p.chunk_states + ((static_cast<int64_t>(b) * n_chunks + tile) * nd + cg * 16) * N;
+#pragma unroll
+    for (int k = 0; k < PPL; ++k)
+      if (pair_valid(k)) cb[pair_offset(k)] = carry[k];
+  };
 
   // Buffer resources of this batch row's x, delta, y, B and C, and the lane's
   // byte offsets of its first step in a tile.
@@ -294,6 +330,7 @@ __global__ __launch_bounds__(64 * W, kMinWavesPerSimd<G>) void ssm_fwd_kernel(Fw
   const rsrc_t ry = make_rsrc(static_cast<char*>(p.y) + b * xd_row, xd_row);
   const rsrc_t rb = make_rsrc(static_cast<const char*>(p.B) + b * bc_row, bc_row);
   const rsrc_t rc = make_rsrc(static_cast<const char*>(p.C) + b * bc_row, bc_row);
+  const rsrc_t rz = make_rsrc(GATE ? static_cast<const char*>(p.z) + b * xd_row : nullptr, GATE ? xd_row : 0);
   const uint32_t off_xd = static_cast<uint32_t>((j * K * nd + d) * E);
   const uint32_t off_bc = static_cast<uint32_t>((j * K * N + 16 * g + c) * E);
 
@@ -348,7 +385,7 @@ __global__ __launch_bounds__(64 * W, kMinWavesPerSimd<G>) void ssm_fwd_kernel(Fw
     float dls[K];
 #pragma unroll
     for (int i = 0; i < K; ++i) {  // delta for all K steps first: covers the B/C load latency
-      float dl = dv[i];
+      float dl = dv[i] + dbias;
       if constexpr (SOFTPLUS) dl = softplus_f32(dl);
       if constexpr (CLAMP) dl = __builtin_amdgcn_fmed3f(dl, p.dmin, p.dmax);
       if constexpr (!FULL) dl = (i < left) ? dl : 0.0f;  // padded step: delta = 0 -> Abar = 1
@@ -381,10 +418,9 @@ __global__ __launch_bounds__(64 * W, kMinWavesPerSimd<G>) void ssm_fwd_kernel(Fw
     // The sub-chunk's decay is a_prod = prod_i exp(delta_i A) = exp2(A log2(e) sum_i delta_i).
 #pragma unroll
     for (int k = 0; k < PPL; ++k) {
-      const int pr = tid + k * NT;
-      if (PAIRS % NT == 0 || pr < PAIRS) {
-        const int cc = pr % 16;  // walk lane -> (channel, state), channel fastest
-        const int n = pr / 16;
+      if (pair_valid(k)) {
+        int cc, n;
+        pair_of(k, cc, n);
         const float a2 = a2s[cc * NS + n];
         float cr = carry[k];
         float* pbw = agg_b[buf] + ((n / 4) * 16 + cc) * 4 + (n % 4);
@@ -398,6 +434,7 @@ __global__ __launch_bounds__(64 * W, kMinWavesPerSimd<G>) void ssm_fwd_kernel(Fw
         carry[k] = cr;
       }
     }
+    store_chunk_state(t_tile / T);
     __syncthreads();
 
     // ---- pass 2: states from the incoming state, readout ----
@@ -423,7 +460,13 @@ __global__ __launch_bounds__(64 * W, kMinWavesPerSimd<G>) void ssm_fwd_kernel(Fw
       float y0 = dskip * xv[i], y1 = 0.0f;
       Unroll<0, 16>::run([&]<int S>() { h[S] = __builtin_fmaf(ab[i][S], h[S], row_bcast<S>(bi) * ui); });
       dot16_row_bcast(y0, y1, cv[i], h);
-      const float yv0 = sum_state_groups<G>(y0 + y1);
+      float yv0 = sum_state_groups<G>(y0 + y1);
+      if constexpr (GATE) {
+        // y * silu(z), silu(z) = z / (1 + 2^(-z log2 e)); padded steps never load z
+        const uint32_t sz = static_cast<uint32_t>((t_tile + i) * xd_step);
+        const float zv = (FULL || i < left) ? Elem<IO>::template load<kStream>(rz, off_xd, sz) : 0.0f;
+        yv0 *= zv * __builtin_amdgcn_rcpf(1.0f + fast_exp2(-zv * kLog2e));
+      }
       const uint32_t sx = static_cast<uint32_t>((t_tile + i) * xd_step);
       if constexpr (FULL) {
         if (G == 1 || (i % G) == g) Elem<IO>::store(ry, off_xd, sx, yv0);
@@ -455,6 +498,7 @@ __global__ __launch_bounds__(64 * W, kMinWavesPerSimd<G>) void ssm_fwd_kernel(Fw
   }
   // Tiles wholly in the padding: the carry is unchanged and y is +0.
   for (; t_next < L; t_next += T) {
+    store_chunk_state(t_next / T);
     const int64_t left = L - t_next - j * K;
 #pragma unroll
     for (int i = 0; i < K; ++i) {
@@ -464,15 +508,10 @@ __global__ __launch_bounds__(64 * W, kMinWavesPerSimd<G>) void ssm_fwd_kernel(Fw
   }
 
   if (p.h_last != nullptr) {
+    float* hb = p.h_last + state_block;
 #pragma unroll
-    for (int k = 0; k < PPL; ++k) {
-      const int pr = tid + k * NT;
-      if (PAIRS % NT == 0 || pr < PAIRS) {
-        const int cc = pr % 16;
-        const int n = pr / 16;
-        p.h_last[(static_cast<int64_t>(b) * nd + cg * 16 + cc) * N + n] = carry[k];
-      }
-    }
+    for (int k = 0; k < PPL; ++k)
+      if (pair_valid(k)) hb[pair_offset(k)] = carry[k];
   }
 }
 
@@ -496,20 +535,45 @@ struct Config<IO, 4> {
   static constexpr int K = 4, W = 8;
 };
 
-template <typename IO, int G, bool SP, bool CL>
+template <typename IO, int G, bool SP, bool CL, bool GATE>
 hipError_t launch_flags(const FwdParams& prm, hipStream_t stream) {
   constexpr int K = Config<IO, G>::K, W = Config<IO, G>::W;
   const int64_t blocks = static_cast<int64_t>(prm.nb) * prm.n_cg;
-  hipLaunchKernelGGL((ssm_fwd_kernel<IO, G, K, W, SP, CL>), dim3(static_cast<unsigned>(blocks)), dim3(64 * W), 0,
-                     stream, prm);
+  hipLaunchKernelGGL((ssm_fwd_kernel<IO, G, K, W, SP, CL, GATE>), dim3(static_cast<unsigned>(blocks)), dim3(64 * W),
+                     0, stream, prm);
   return hipGetLastError();
+}
+
+template <typename IO, int G, bool SP>
+hipError_t launch_sp(const FwdParams& prm, hipStream_t stream) {
+  const bool gate = prm.z != nullptr;
+  if (prm.clamp)
+    return gate ? launch_flags<IO, G, SP, true, true>(prm, stream) : launch_flags<IO, G, SP, true, false>(prm, stream);
+  return gate ? launch_flags<IO, G, SP, false, true>(prm, stream) : launch_flags<IO, G, SP, false, false>(prm, stream);
 }
 
 template <typename IO, int G>
 hipError_t launch(const FwdParams& prm, hipStream_t stream) {
-  if (prm.softplus)
-    return prm.clamp ? launch_flags<IO, G, true, true>(prm, stream) : launch_flags<IO, G, true, false>(prm, stream);
-  return prm.clamp ? launch_flags<IO, G, false, true>(prm, stream) : launch_flags<IO, G, false, false>(prm, stream);
+  return prm.softplus ? launch_sp<IO, G, true>(prm, stream) : launch_sp<IO, G, false>(prm, stream);
+}
+
+// Steps per time tile of the kernel for state count N (= chunk_len of the
+// chunk-boundary states): W waves x (4 / G) sub-chunks per wave x K steps.
+template <int G>
+constexpr int64_t tile_steps_g = Config<uint16_t, G>::W * (4 / G) * Config<uint16_t, G>::K;
+static_assert(tile_steps_g<1> == Config<float, 1>::W * 4 * Config<float, 1>::K, "tile must not depend on io");
+
+int64_t tile_steps(int64_t N) {
+  switch (N) {
+    case 16:
+      return tile_steps_g<1>;
+    case 32:
+      return tile_steps_g<2>;
+    case 64:
+      return tile_steps_g<4>;
+    default:
+      return 0;
+  }
 }
 
 template <typename IO>
@@ -524,10 +588,10 @@ hipError_t launch_io(int G, const FwdParams& prm, hipStream_t stream) {
   }
 }
 
-// Zero-fills h_last when there are no time steps.
-__global__ void zero_fill_kernel(float* p, int64_t n) {
+// h_last when there are no time steps: a copy of h0, or zeros.
+__global__ void copy_fill_kernel(float* dst, const float* src, int64_t n) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < n) p[i] = 0.0f;
+  if (i < n) dst[i] = (src != nullptr) ? src[i] : 0.0f;
 }
 
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
@@ -596,12 +660,14 @@ const char* ssm_scan_error_string(int code) {
   }
 }
 
+int64_t ssm_scan_chunk_len(int64_t dstate) { return tile_steps(dstate); }
+
 // Checks run in this order: dims, sizes and flags; pointers; alignment;
 // aliasing; the handle; the current device.  Nothing is enqueued unless all
 // pass.
-int ssm_selective_scan_fwd(ssm_scan_t handle, const void* x, const void* delta, const float* A_log, const void* B,
-                           const void* C, const float* D, const int32_t* valid_len, void* y, float* h_last,
-                           const ssm_scan_dims* dims, void* stream) {
+int ssm_selective_scan_fwd_ex(ssm_scan_t handle, const void* x, const void* delta, const float* A_log, const void* B,
+                              const void* C, const float* D, const int32_t* valid_len, void* y, float* h_last,
+                              const ssm_scan_dims* dims, const ssm_scan_fwd_extras* extras, void* stream) {
   if (dims == nullptr) return SSM_ERR_INVALID_ARG;
   const int64_t nb = dims->batch, L = dims->seqlen, nd = dims->dim, N = dims->dstate;
   if (nb < 0 || L < 0 || nd < 0 || N < 0) return SSM_ERR_INVALID_ARG;
@@ -617,29 +683,45 @@ int ssm_selective_scan_fwd(ssm_scan_t handle, const void* x, const void* delta, 
   // indices are 64-bit in the kernel.
   if (nb > 0 && nd > 0 && (nb * (nd / 16) > 0x7fffffffLL || nb > 0x7fffffffLL || nd > 0x7fffffffLL))
     return SSM_ERR_UNSUPPORTED;
-  // A batch row of x, delta, y, B or C must span fewer than 2^31 bytes (it is
-  // addressed through one buffer resource with 32-bit offsets).
+  // A batch row of x, delta, y, z, B or C must span fewer than 2^31 bytes (it
+  // is addressed through one buffer resource with 32-bit offsets).
   const int64_t esz = dims->io_dtype == SSM_IO_BF16 ? 2 : 4;
   if (L > 0 && L * (N > nd ? N : nd) * esz > 0x7fffffffLL) return SSM_ERR_UNSUPPORTED;
 
+  const ssm_scan_fwd_extras none = {nullptr, nullptr, nullptr, nullptr, 0};
+  const ssm_scan_fwd_extras& ex = extras ? *extras : none;
+  if (ex.chunk_states != nullptr && ex.chunk_len != tile_steps(N)) return SSM_ERR_INVALID_ARG;
+
   const bool empty = (nb == 0 || nd == 0);
-  const size_t e = dims->io_dtype == SSM_IO_BF16 ? 2 : 4;
+  const size_t e = static_cast<size_t>(esz);
   const size_t n_xd = static_cast<size_t>(nb) * L * nd, n_bc = static_cast<size_t>(nb) * L * N;
+  const size_t n_state = static_cast<size_t>(nb) * nd * N;
+  const size_t n_chunks = L > 0 ? static_cast<size_t>((L + tile_steps(N) - 1) / tile_steps(N)) : 0;
   if (!empty) {
     if (A_log == nullptr) return SSM_ERR_INVALID_ARG;
     if (L > 0 && (x == nullptr || delta == nullptr || B == nullptr || C == nullptr || y == nullptr))
       return SSM_ERR_INVALID_ARG;
     if (!aligned(x, e) || !aligned(delta, e) || !aligned(B, e) || !aligned(C, e) || !aligned(y, e) ||
-        !aligned(A_log, 4) || !aligned(D, 4) || !aligned(valid_len, 4) || !aligned(h_last, 4))
+        !aligned(ex.z, e) || !aligned(A_log, 4) || !aligned(D, 4) || !aligned(valid_len, 4) || !aligned(h_last, 4) ||
+        !aligned(ex.h0, 4) || !aligned(ex.delta_bias, 4) || !aligned(ex.chunk_states, 4))
       return SSM_ERR_UNSUPPORTED;
-    const size_t by = L > 0 ? n_xd * e : 0, bh = h_last ? static_cast<size_t>(nb) * nd * N * 4 : 0;
-    const void* ins[] = {x, delta, B, C, A_log, D, valid_len};
+    const size_t by = L > 0 ? n_xd * e : 0, bh = h_last ? n_state * 4 : 0;
+    const size_t bcs = ex.chunk_states ? n_chunks * n_state * 4 : 0;
+    const void* ins[] = {x, delta, B, C, A_log, D, valid_len, L > 0 ? ex.z : nullptr, ex.h0, ex.delta_bias};
     const size_t ins_n[] = {n_xd * e, n_xd * e, n_bc * e, n_bc * e, static_cast<size_t>(nd) * N * 4,
-                            D ? static_cast<size_t>(nd) * 4 : 0, valid_len ? static_cast<size_t>(nb) * 4 : 0};
-    for (int k = 0; k < 7; ++k) {
-      if (overlaps(y, by, ins[k], ins_n[k]) || overlaps(h_last, bh, ins[k], ins_n[k])) return SSM_ERR_ALIAS;
+                            D ? static_cast<size_t>(nd) * 4 : 0, valid_len ? static_cast<size_t>(nb) * 4 : 0,
+                            ex.z ? n_xd * e : 0, ex.h0 ? n_state * 4 : 0, ex.delta_bias ? static_cast<size_t>(nd) * 4 : 0};
+    for (int k = 0; k < 10; ++k) {
+      // h0 may be h_last itself: each state element is read before the same
+      // thread overwrites it.
+      const bool h0_in_place = (ins[k] == ex.h0 && ex.h0 != nullptr && static_cast<const void*>(h_last) == ex.h0);
+      if (overlaps(y, by, ins[k], ins_n[k]) || overlaps(ex.chunk_states, bcs, ins[k], ins_n[k]))
+        return SSM_ERR_ALIAS;
+      if (!h0_in_place && overlaps(h_last, bh, ins[k], ins_n[k])) return SSM_ERR_ALIAS;
     }
-    if (overlaps(y, by, h_last, bh)) return SSM_ERR_ALIAS;
+    if (overlaps(y, by, h_last, bh) || overlaps(y, by, ex.chunk_states, bcs) ||
+        overlaps(h_last, bh, ex.chunk_states, bcs))
+      return SSM_ERR_ALIAS;
   }
   if (handle == nullptr) return SSM_ERR_INVALID_ARG;
   int cur = -1;
@@ -652,9 +734,17 @@ int ssm_selective_scan_fwd(ssm_scan_t handle, const void* x, const void* delta, 
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (L == 0) {
+    // No steps: the final state is the initial one.
     if (h_last == nullptr) return SSM_OK;
     const int64_t n = nb * nd * N;
-    hipLaunchKernelGGL(zero_fill_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, h_last, n);
+    if (ex.h0 != nullptr) {
+      if (ex.h0 == h_last) return SSM_OK;
+      hipLaunchKernelGGL(copy_fill_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, h_last,
+                         ex.h0, n);
+    } else {
+      hipLaunchKernelGGL(copy_fill_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, h_last,
+                         static_cast<const float*>(nullptr), n);
+    }
     return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
   }
 
@@ -668,6 +758,10 @@ int ssm_selective_scan_fwd(ssm_scan_t handle, const void* x, const void* delta, 
   prm.valid_len = valid_len;
   prm.y = y;
   prm.h_last = h_last;
+  prm.h0 = ex.h0;
+  prm.delta_bias = ex.delta_bias;
+  prm.z = ex.z;
+  prm.chunk_states = ex.chunk_states;
   prm.L = L;
   prm.nb = static_cast<int32_t>(nb);
   prm.nd = static_cast<int32_t>(nd);
@@ -680,6 +774,12 @@ int ssm_selective_scan_fwd(ssm_scan_t handle, const void* x, const void* delta, 
   const hipError_t err =
       dims->io_dtype == SSM_IO_BF16 ? launch_io<uint16_t>(G, prm, s) : launch_io<float>(G, prm, s);
   return err == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+int ssm_selective_scan_fwd(ssm_scan_t handle, const void* x, const void* delta, const float* A_log, const void* B,
+                           const void* C, const float* D, const int32_t* valid_len, void* y, float* h_last,
+                           const ssm_scan_dims* dims, void* stream) {
+  return ssm_selective_scan_fwd_ex(handle, x, delta, A_log, B, C, D, valid_len, y, h_last, dims, nullptr, stream);
 }
 
 }  // extern "C"

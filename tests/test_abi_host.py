@@ -102,6 +102,32 @@ def test_aliasing():
     assert call(_dims(), y=7 * MB - 2 * 8 * 16 * 2) == ssm.SSM_ERR_INVALID_ARG
 
 
+def _ex_call(dims, extras, **over):
+    p = dict(PTRS, **over)
+    return ssm.ssm_selective_scan_fwd_ex(None, p["x"], p["delta"], p["A_log"], p["B"], p["C"], p["D"],
+                                         p["valid_len"], p["y"], p["h_last"], dims, extras, None)
+
+
+def test_extras_checks():
+    E = ssm.ssm_scan_fwd_extras
+    assert ssm.chunk_len(16) == 128 and ssm.chunk_len(32) == 64 and ssm.chunk_len(64) == 32
+    assert ssm.chunk_len(8) == 0
+    # NULL extras and all-NULL extras reach the handle check
+    assert _ex_call(_dims(), None) == ssm.SSM_ERR_INVALID_ARG
+    assert _ex_call(_dims(), E()) == ssm.SSM_ERR_INVALID_ARG
+    # chunk states need the kernel's chunk length
+    assert _ex_call(_dims(), E(chunk_states=8 * MB, chunk_len=64)) == ssm.SSM_ERR_INVALID_ARG
+    # misaligned extras
+    assert _ex_call(_dims(), E(h0=8 * MB + 2)) == ssm.SSM_ERR_UNSUPPORTED
+    assert _ex_call(_dims(io=ssm.SSM_IO_BF16), E(z=8 * MB + 1)) == ssm.SSM_ERR_UNSUPPORTED
+    # outputs must not overlap the extra inputs; h0 may be h_last itself
+    assert _ex_call(_dims(), E(z=PTRS["y"])) == ssm.SSM_ERR_ALIAS
+    assert _ex_call(_dims(), E(h0=PTRS["h_last"] + 4)) == ssm.SSM_ERR_ALIAS
+    assert _ex_call(_dims(), E(h0=PTRS["h_last"])) == ssm.SSM_ERR_INVALID_ARG  # in place: reaches the handle check
+    assert _ex_call(_dims(), E(chunk_states=PTRS["x"], chunk_len=128)) == ssm.SSM_ERR_ALIAS
+    assert _ex_call(_dims(), E(chunk_states=PTRS["h_last"], chunk_len=128)) == ssm.SSM_ERR_ALIAS
+
+
 def test_empty_problem_needs_only_the_handle():
     assert call(_dims(batch=0), x=None, delta=None, B=None, C=None, y=None, A_log=None) == ssm.SSM_ERR_INVALID_ARG
 
