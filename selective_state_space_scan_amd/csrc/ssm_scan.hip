@@ -148,32 +148,33 @@ __device__ __forceinline__ float row_bcast(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + S, 0xf, 0xf, true));
 }
 
-// y0 += C[s] * h[s] (even s), y1 += C[s] * h[s] (odd s) over the 16 states,
-// C[s] taken from lane s of the row by DPP row_newbcast fused into v_fmac_f32
-// (the compiler does not fuse a DPP move into v_fmac, so this is written out).
-// The leading s_nop covers the DPP hazards (a VALU write of the DPP source
-// needs 2 wait states before the read, a VALU write of EXEC needs 5); c is not
-// written inside the block.
-__device__ __forceinline__ void dot16_row_bcast(float& y0, float& y1, float c, const float (&h)[16]) {
+// y_m += C[s] * h[s] for s % 4 == m over the 16 states (four accumulators, so
+// that consecutive instructions do not depend on each other), C[s] taken from
+// lane s of the row by DPP row_newbcast fused into v_fmac_f32 (the compiler
+// does not fuse a DPP move into v_fmac, so this is written out).  The leading
+// s_nop covers the DPP hazards (a VALU write of the DPP source needs 2 wait
+// states before the read, a VALU write of EXEC needs 5); c is not written
+// inside the block.
+__device__ __forceinline__ void dot16_row_bcast(float (&y)[4], float c, const float (&h)[16]) {
   asm volatile(
       "s_nop 4\n\t"
-      "v_fmac_f32_dpp %0, %2, %3 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
-      "v_fmac_f32_dpp %1, %2, %4 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
-      "v_fmac_f32_dpp %0, %2, %5 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
-      "v_fmac_f32_dpp %1, %2, %6 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
-      "v_fmac_f32_dpp %0, %2, %7 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
-      "v_fmac_f32_dpp %1, %2, %8 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
-      "v_fmac_f32_dpp %0, %2, %9 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
-      "v_fmac_f32_dpp %1, %2, %10 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
-      "v_fmac_f32_dpp %0, %2, %11 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
-      "v_fmac_f32_dpp %1, %2, %12 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
-      "v_fmac_f32_dpp %0, %2, %13 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
-      "v_fmac_f32_dpp %1, %2, %14 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
-      "v_fmac_f32_dpp %0, %2, %15 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
-      "v_fmac_f32_dpp %1, %2, %16 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
-      "v_fmac_f32_dpp %0, %2, %17 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
-      "v_fmac_f32_dpp %1, %2, %18 row_newbcast:15 row_mask:0xf bank_mask:0xf"
-      : "+v"(y0), "+v"(y1)
+      "v_fmac_f32_dpp %0, %4, %5 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %4, %6 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %4, %7 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %4, %8 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %4, %9 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %4, %10 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %4, %11 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %4, %12 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %4, %13 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %4, %14 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %4, %15 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %4, %16 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %4, %17 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %4, %18 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %4, %19 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %4, %20 row_newbcast:15 row_mask:0xf bank_mask:0xf"
+      : "+v"(y[0]), "+v"(y[1]), "+v"(y[2]), "+v"(y[3])
       : "v"(c), "v"(h[0]), "v"(h[1]), "v"(h[2]), "v"(h[3]), "v"(h[4]), "v"(h[5]), "v"(h[6]), "v"(h[7]),
         "v"(h[8]), "v"(h[9]), "v"(h[10]), "v"(h[11]), "v"(h[12]), "v"(h[13]), "v"(h[14]), "v"(h[15]));
 }
@@ -231,6 +232,8 @@ __global__ __launch_bounds__(64 * W, kMinWavesPerSimd<G>) void ssm_fwd_kernel(Fw
   constexpr int SUB = W * QR;           // sub-chunks per tile
   constexpr int T = SUB * K;            // steps per tile
   constexpr int NS = N + 4;             // padded row stride of the A table in floats
+  constexpr int SDS = SUB + 4;          // padded row stride of the sub-chunk delta sums
+  static_assert(SUB % 4 == 0, "sub-chunk records are read as quads");
   constexpr int AGG = SUB * 16 * N;     // floats of one tile's sub-chunk records
   constexpr int PAIRS = 16 * N;         // (channel, state) pairs of the workgroup
   constexpr int NT = 64 * W;            // threads
@@ -245,7 +248,9 @@ __global__ __launch_bounds__(64 * W, kMinWavesPerSimd<G>) void ssm_fwd_kernel(Fw
   // alternate between tiles, so the next tile's pass 1 may write while the
   // previous one is still being read.
   __shared__ __attribute__((aligned(16))) float agg_b[2][AGG];
-  __shared__ float agg_sd[2][SUB * 16];   // sum of delta over each sub-chunk, per channel
+  // Sum of delta over each sub-chunk, channel-major (row stride SDS) so that a
+  // walk lane reads its channel's sub-chunks as consecutive quads.
+  __shared__ __attribute__((aligned(16))) float agg_sd[2][16 * SDS];
   __shared__ __attribute__((aligned(16))) float a2s[16 * NS];  // A * log2(e) for the workgroup's channels
 
   // Workgroup -> (batch row, channel group).  Workgroups are dealt to the 8
@@ -410,7 +415,7 @@ __global__ __launch_bounds__(64 * W, kMinWavesPerSimd<G>) void ssm_fwd_kernel(Fw
 #pragma unroll
       for (int s = 0; s < 16; s += 4)
         *reinterpret_cast<float4*>(pb + s * 16) = make_float4(bt[s], bt[s + 1], bt[s + 2], bt[s + 3]);
-      if (g == 0) agg_sd[buf][j * 16 + c] = sd;
+      if (g == 0) agg_sd[buf][c * SDS + j] = sd;
     }
     __syncthreads();
 
@@ -424,12 +429,31 @@ __global__ __launch_bounds__(64 * W, kMinWavesPerSimd<G>) void ssm_fwd_kernel(Fw
         const float a2 = a2s[cc * NS + n];
         float cr = carry[k];
         float* pbw = agg_b[buf] + ((n / 4) * 16 + cc) * 4 + (n % 4);
-#pragma unroll 8
-        for (int jj = 0; jj < SUB; ++jj) {
-          const float a = fast_exp2(a2 * agg_sd[buf][jj * 16 + cc]);
-          const float bb = pbw[jj * (N / 4) * 64];
-          pbw[jj * (N / 4) * 64] = cr;
-          cr = __builtin_fmaf(a, cr, bb);
+        const float* psd = agg_sd[buf] + cc * SDS;
+        // Batches of WB sub-chunks: all LDS reads of a batch are issued
+        // together and the decays computed off the carry chain, so the
+        // serial part is one FMA and one LDS write per sub-chunk.
+        constexpr int WB = SUB < 8 ? SUB : 8;
+#pragma unroll
+        for (int j0 = 0; j0 < SUB; j0 += WB) {
+          float av[WB], bb[WB];
+#pragma unroll
+          for (int u = 0; u < WB; u += 4) {
+            const float4 v = *reinterpret_cast<const float4*>(psd + j0 + u);
+            av[u] = v.x;
+            av[u + 1] = v.y;
+            av[u + 2] = v.z;
+            av[u + 3] = v.w;
+          }
+#pragma unroll
+          for (int u = 0; u < WB; ++u) bb[u] = pbw[(j0 + u) * (N / 4) * 64];
+#pragma unroll
+          for (int u = 0; u < WB; ++u) av[u] = fast_exp2(a2 * av[u]);
+#pragma unroll
+          for (int u = 0; u < WB; ++u) {
+            pbw[(j0 + u) * (N / 4) * 64] = cr;
+            cr = __builtin_fmaf(av[u], cr, bb[u]);
+          }
         }
         carry[k] = cr;
       }
@@ -457,10 +481,10 @@ __global__ __launch_bounds__(64 * W, kMinWavesPerSimd<G>) void ssm_fwd_kernel(Fw
       float bi = bv[i];
       asm volatile("" : "+v"(bi));
       const float ui = u[i];
-      float y0 = dskip * xv[i], y1 = 0.0f;
+      float ya[4] = {dskip * xv[i], 0.0f, 0.0f, 0.0f};
       Unroll<0, 16>::run([&]<int S>() { h[S] = __builtin_fmaf(ab[i][S], h[S], row_bcast<S>(bi) * ui); });
-      dot16_row_bcast(y0, y1, cv[i], h);
-      float yv0 = sum_state_groups<G>(y0 + y1);
+      dot16_row_bcast(ya, cv[i], h);
+      float yv0 = sum_state_groups<G>((ya[0] + ya[1]) + (ya[2] + ya[3]));
       if constexpr (GATE) {
         // y * silu(z), silu(z) = z / (1 + 2^(-z log2 e)); padded steps never load z
         const uint32_t sz = static_cast<uint32_t>((t_tile + i) * xd_step);
