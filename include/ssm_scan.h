@@ -113,18 +113,52 @@ int ssm_selective_scan_fwd(ssm_scan_t handle, const void* x, const void* delta, 
  *               chunk may be shorter; past valid_len the state no longer
  *               changes) -- the boundary states kept for recomputation in the
  *               pwwt.cn article, section 3.4.
- *  chunk_len    must equal ssm_scan_chunk_len(dstate) when chunk_states is set. */
+ *  chunk_len    must equal ssm_scan_chunk_len(dstate) when chunk_states is set.
+ *
+ *  time_parts, workspace, workspace_bytes: cut the time axis into parts that
+ *               run on different workgroups (the multi-block chunked scan of
+ *               the pwwt.cn article, sections 3.1 and 4.2: each block folds its
+ *               chunk, the chunk carries are combined in order, each chunk is
+ *               then rescanned from its incoming state), for batches too small
+ *               to fill the GPU with (row, channel) work alone.  Two kernels
+ *               run on the stream: the fold of the first P-1 parts, then every
+ *               part.  time_parts = 0 lets the library choose
+ *               (ssm_scan_auto_time_parts) and falls back to no split when the
+ *               workspace is NULL or smaller than ssm_scan_workspace_bytes for
+ *               that choice; 1 never splits; P >= 2 asks for at most P parts
+ *               of whole chunks and needs at least
+ *               ssm_scan_workspace_bytes(dims, P) bytes of device workspace
+ *               (else SSM_ERR_INVALID_ARG).  The workspace is caller-owned
+ *               scratch (4-byte aligned, overlapping nothing else) that the
+ *               call overwrites; it must not be shared by calls that may run
+ *               at the same time.  With two parts the results are bitwise those
+ *               of the unsplit scan; with more, the states entering parts 2 and
+ *               later are composed from per-part sums and may differ from
+ *               them by rounding. */
 typedef struct ssm_scan_fwd_extras {
   const float* h0;
   const float* delta_bias;
   const void* z;
   float* chunk_states;
   int64_t chunk_len;
+  int32_t time_parts;
+  void* workspace;
+  int64_t workspace_bytes;
 } ssm_scan_fwd_extras;
 
 /* Steps per chunk of chunk_states for this dstate (the kernel's time tile):
  * 128, 64 or 32 for dstate 16, 32 or 64; 0 for an unsupported dstate. */
 int64_t ssm_scan_chunk_len(int64_t dstate);
+
+/* The number of time parts the library picks for these dims on the handle's
+ * GPU when time_parts = 0 (1 = no split).  Returns 1 for a NULL handle or
+ * dims, or invalid sizes. */
+int32_t ssm_scan_auto_time_parts(ssm_scan_t handle, const ssm_scan_dims* dims);
+
+/* Bytes of workspace a split into (at most) time_parts parts needs for these
+ * dims (0 when that split is no split); -1 for NULL dims, a negative size or
+ * time_parts, or an unsupported dstate. */
+int64_t ssm_scan_workspace_bytes(const ssm_scan_dims* dims, int32_t time_parts);
 
 /* ssm_selective_scan_fwd with the optional extras above (extras may be NULL,
  * which is ssm_selective_scan_fwd).  Same ordering, asynchrony and errors;

@@ -26,7 +26,7 @@ SSM_IO_BF16 = 1
 
 # Names declared in include/ssm_scan.h.
 EXPORTED = ("ssm_scan_create", "ssm_selective_scan_fwd", "ssm_selective_scan_fwd_ex", "ssm_scan_chunk_len",
-            "ssm_scan_destroy", "ssm_scan_error_string")
+            "ssm_scan_auto_time_parts", "ssm_scan_workspace_bytes", "ssm_scan_destroy", "ssm_scan_error_string")
 
 
 class SsmScanError(RuntimeError):
@@ -56,6 +56,9 @@ class ssm_scan_fwd_extras(ctypes.Structure):
         ("z", ctypes.c_void_p),
         ("chunk_states", ctypes.c_void_p),
         ("chunk_len", ctypes.c_int64),
+        ("time_parts", ctypes.c_int32),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_int64),
     ]
 
 
@@ -77,6 +80,11 @@ def lib() -> ctypes.CDLL:
             raise ImportError(
                 f"HIP library not built: {LIB_PATH} is missing; run "
                 "`python -m selective_state_space_scan_amd.build` (or __graft_entry__.build())")
+        # torch ships its own HIP runtime under the same soname as the system
+        # one the library links against; loading torch first makes the library
+        # bind to that copy, so the process holds a single HIP runtime whatever
+        # the import order of the caller.
+        import torch  # noqa: F401
         L = ctypes.CDLL(LIB_PATH)
         vp = ctypes.c_void_p
         L.ssm_scan_create.argtypes = [ctypes.POINTER(vp), ctypes.c_int]
@@ -93,6 +101,10 @@ def lib() -> ctypes.CDLL:
         L.ssm_selective_scan_fwd_ex.restype = ctypes.c_int
         L.ssm_scan_chunk_len.argtypes = [ctypes.c_int64]
         L.ssm_scan_chunk_len.restype = ctypes.c_int64
+        L.ssm_scan_auto_time_parts.argtypes = [vp, ctypes.POINTER(ssm_scan_dims)]
+        L.ssm_scan_auto_time_parts.restype = ctypes.c_int32
+        L.ssm_scan_workspace_bytes.argtypes = [ctypes.POINTER(ssm_scan_dims), ctypes.c_int32]
+        L.ssm_scan_workspace_bytes.restype = ctypes.c_int64
         _lib = L
         return L
 
@@ -137,6 +149,16 @@ def chunk_len(dstate: int) -> int:
     return int(lib().ssm_scan_chunk_len(int(dstate)))
 
 
+def auto_time_parts(handle, dims: ssm_scan_dims) -> int:
+    """The time split the library picks for these dims on the handle's GPU."""
+    return int(lib().ssm_scan_auto_time_parts(handle, ctypes.byref(dims)))
+
+
+def workspace_bytes(dims: ssm_scan_dims, time_parts: int) -> int:
+    """Device workspace bytes a split into (at most) time_parts parts needs."""
+    return int(lib().ssm_scan_workspace_bytes(ctypes.byref(dims), int(time_parts)))
+
+
 # ---- torch front end -----------------------------------------------------
 
 _handles: dict[int, int] = {}
@@ -154,7 +176,7 @@ def handle_for(device_index: int) -> int:
 
 def selective_scan_fwd(x, delta, A_log, B, C, D=None, valid_len=None, *, delta_softplus: bool = True,
                        delta_clamp=None, y=None, h_last=None, return_h_last: bool = True, h0=None, delta_bias=None,
-                       z=None, return_chunk_states: bool = False, stream=None):
+                       z=None, return_chunk_states: bool = False, time_parts=None, workspace=None, stream=None):
     """Selective-scan forward on the GPU.  Returns ``(y, h_last)``, or
     ``(y, h_last, chunk_states)`` with ``return_chunk_states``.
 
@@ -170,6 +192,11 @@ def selective_scan_fwd(x, delta, A_log, B, C, D=None, valid_len=None, *, delta_s
     itself); delta_bias [dim] float32 added to delta before softplus; z like x,
     output gate y * silu(z); chunk states [batch, ceil(L / chunk_len(dstate)),
     dim, dstate] float32, the state after every chunk.
+
+    Time split: ``time_parts`` None lets the library choose (it splits only
+    batches too small to fill the GPU), 1 never splits, P >= 2 asks for at most
+    P parts.  ``workspace`` is an optional contiguous uint8 tensor on x's device
+    used as scratch for a split; one is allocated when needed and not given.
     """
     import torch
 
@@ -234,12 +261,26 @@ def selective_scan_fwd(x, delta, A_log, B, C, D=None, valid_len=None, *, delta_s
     def ptr(t):
         return None if t is None or t.numel() == 0 else t.data_ptr()
 
-    extras = None
-    if h0 is not None or delta_bias is not None or z is not None or chunk_states is not None:
-        extras = ssm_scan_fwd_extras(ptr(h0), ptr(delta_bias), ptr(z), ptr(chunk_states),
-                                     cl if chunk_states is not None else 0)
     with torch.cuda.device(dev):
         h = handle_for(dev.index if dev.index is not None else torch.cuda.current_device())
+        parts = auto_time_parts(h, dims) if time_parts is None else int(time_parts)
+        if parts < 1:
+            raise ValueError("time_parts must be None or >= 1")
+        ws_bytes = workspace_bytes(dims, parts) if parts >= 2 else 0
+        if ws_bytes > 0:
+            if workspace is None:
+                workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+                if hasattr(stream, "cuda_stream"):
+                    workspace.record_stream(stream)  # freed only after the stream's work
+            elif (workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous()
+                  or workspace.numel() < ws_bytes):
+                raise ValueError(f"workspace must be a contiguous uint8 tensor of at least {ws_bytes} bytes on {dev}")
+        extras = None
+        if (h0 is not None or delta_bias is not None or z is not None or chunk_states is not None
+                or ws_bytes > 0 or time_parts is not None):
+            extras = ssm_scan_fwd_extras(ptr(h0), ptr(delta_bias), ptr(z), ptr(chunk_states),
+                                         cl if chunk_states is not None else 0, parts,
+                                         ptr(workspace) if ws_bytes > 0 else None, ws_bytes)
         if extras is None:
             rc = ssm_selective_scan_fwd(h, ptr(x), ptr(delta), ptr(A_log), ptr(B), ptr(C), ptr(D), ptr(valid_len),
                                         ptr(y), ptr(h_last), dims, sptr)

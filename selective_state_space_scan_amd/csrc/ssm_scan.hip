@@ -65,6 +65,12 @@ struct FwdParams {
   const float* delta_bias;
   const void* z;
   float* chunk_states;
+  // Time split across workgroups: the sequence is cut into n_parts parts of
+  // part_len steps (a multiple of the tile; part_len = L when unsplit).  ws
+  // holds, per part boundary, what the fold kernel leaves for the next parts.
+  float* ws;
+  int64_t part_len;
+  int32_t n_parts;
   int64_t L;
   int32_t nb;
   int32_t nd;
@@ -225,8 +231,13 @@ struct Unroll<K, K> {
 template <int G>
 constexpr int kMinWavesPerSimd = (G == 1) ? 4 : 2;
 
-template <typename IO, int G, int K, int W, bool SOFTPLUS, bool CLAMP, bool GATE>
-__global__ __launch_bounds__(64 * W, kMinWavesPerSimd<G>) void ssm_fwd_kernel(FwdParams p) {
+// FOLD: the fold kernel of the time split -- pass 1 and the carry walk only,
+// over parts 0 .. n_parts-2, leaving each part's carry-out (part 0, from h0)
+// or its b_total and delta sum (later parts, from zero) in the workspace.
+// Otherwise the full forward over every part, each starting from the state
+// the workspace gives for its first step.
+template <typename IO, int G, int K, int W, bool SOFTPLUS, bool CLAMP, bool GATE, bool FOLD>
+__global__ __launch_bounds__(64 * W, FOLD ? 4 : kMinWavesPerSimd<G>) void ssm_fwd_kernel(FwdParams p) {
   constexpr int N = 16 * G;             // states per channel
   constexpr int QR = 4 / G;             // time sub-chunks per wave
   constexpr int SUB = W * QR;           // sub-chunks per tile
@@ -253,15 +264,17 @@ __global__ __launch_bounds__(64 * W, kMinWavesPerSimd<G>) void ssm_fwd_kernel(Fw
   __shared__ __attribute__((aligned(16))) float agg_sd[2][16 * SDS];
   __shared__ __attribute__((aligned(16))) float a2s[16 * NS];  // A * log2(e) for the workgroup's channels
 
-  // Workgroup -> (batch row, channel group).  Workgroups are dealt to the 8
-  // XCDs round-robin; consecutive logical ids are kept on one XCD so that
-  // neighbouring channel groups (which share 128-byte lines of x, delta and y)
-  // share that XCD's L2.
-  const int64_t total = static_cast<int64_t>(p.nb) * p.n_cg;
+  // Workgroup -> (time part, batch row, channel group).  Workgroups are dealt
+  // to the 8 XCDs round-robin; consecutive logical ids are kept on one XCD so
+  // that neighbouring channel groups (which share 128-byte lines of x, delta
+  // and y) share that XCD's L2.
+  const int64_t groups = static_cast<int64_t>(p.nb) * p.n_cg;
+  const int64_t total = groups * (FOLD ? p.n_parts - 1 : p.n_parts);
   const int64_t bid = blockIdx.x;
   const int64_t per_xcd = total / 8;
   const int64_t logical = (bid < per_xcd * 8) ? (bid % 8) * per_xcd + bid / 8 : bid;
-  const int b = static_cast<int>(logical / p.n_cg);
+  const int part = static_cast<int>(logical / groups);
+  const int b = static_cast<int>((logical % groups) / p.n_cg);
   const int cg = static_cast<int>(logical % p.n_cg);
 
   const int tid = threadIdx.x;
@@ -273,14 +286,19 @@ __global__ __launch_bounds__(64 * W, kMinWavesPerSimd<G>) void ssm_fwd_kernel(Fw
   const int g = r % G;
   const int j = w * QR + q;  // sub-chunk index within the tile
   const int d = cg * 16 + c;
-  const int64_t L = p.L;
   const int nd = p.nd;
+  // This workgroup's steps [t_begin, t_begin + L) of the sequence; below, every
+  // step index is relative to t_begin.
+  const int64_t t_begin = part * p.part_len;
+  const int64_t L = (p.L - t_begin < p.part_len) ? p.L - t_begin : p.part_len;
 
-  int64_t len = L;
+  int64_t len = p.L;  // valid steps of the row, then of the part
   if (p.valid_len != nullptr) {
     const int64_t v = p.valid_len[b];
-    len = v < 0 ? 0 : (v > L ? L : v);
+    len = v < 0 ? 0 : (v > p.L ? p.L : v);
   }
+  len = len - t_begin;
+  len = len < 0 ? 0 : (len > L ? L : len);
 
   for (int k = tid; k < 16 * N; k += NT) {
     const int cc = k / N, n = k % N;
@@ -305,21 +323,51 @@ __global__ __launch_bounds__(64 * W, kMinWavesPerSimd<G>) void ssm_fwd_kernel(Fw
     return static_cast<uint32_t>(cc * N + n);
   };
   const int64_t state_block = (static_cast<int64_t>(b) * nd + cg * 16) * N;
+  // Workspace: n_parts - 1 state blocks [nb, nd, N] -- block 0 is the state
+  // entering part 1, block q >= 1 the b_total of part q folded from zero --
+  // then the delta sums of parts 1 .. n_parts-2, [n_parts - 2, nb, nd].
+  const int64_t ws_block = static_cast<int64_t>(p.nb) * nd * N;
+  float* const ws_sd = p.ws + (p.n_parts - 1) * ws_block;
 
   float carry[PPL];
 #pragma unroll
   for (int k = 0; k < PPL; ++k) carry[k] = 0.0f;
-  if (p.h0 != nullptr) {
-    const float* h0b = p.h0 + state_block;
+  if (part == 0) {
+    if (p.h0 != nullptr) {
+      const float* h0b = p.h0 + state_block;
 #pragma unroll
-    for (int k = 0; k < PPL; ++k)
-      if (pair_valid(k)) carry[k] = h0b[pair_offset(k)];
+      for (int k = 0; k < PPL; ++k)
+        if (pair_valid(k)) carry[k] = h0b[pair_offset(k)];
+    }
+  } else if (!FOLD) {
+    // The state entering this part: the carry into part 1, then the parts in
+    // between composed as affine maps (a_prod = exp2(A log2(e) sum(delta)),
+    // b_total), in time order -- the chunk-to-chunk carry of the chunked scan.
+#pragma unroll
+    for (int k = 0; k < PPL; ++k) {
+      if (pair_valid(k)) {
+        int cc, n;
+        pair_of(k, cc, n);
+        const float a2 = -expf(p.A_log[static_cast<int64_t>(cg * 16 + cc) * N + n]) * kLog2e;
+        float cr = p.ws[state_block + pair_offset(k)];
+        for (int qp = 1; qp < part; ++qp) {
+          const float sdq = ws_sd[(static_cast<int64_t>(qp - 1) * p.nb + b) * nd + cg * 16 + cc];
+          cr = __builtin_fmaf(fast_exp2(a2 * sdq), cr, p.ws[qp * ws_block + state_block + pair_offset(k)]);
+        }
+        carry[k] = cr;
+      }
+    }
   }
-  // Chunk-boundary states: the carry after each tile.
-  const int64_t n_chunks = (L + T - 1) / T;
+  float part_sd[PPL];  // FOLD, part >= 1: the part's delta sum for the pair's channel
+#pragma unroll
+  for (int k = 0; k < PPL; ++k) part_sd[k] = 0.0f;
+  // Chunk-boundary states: the carry after each tile (tiles are numbered from
+  // the start of the sequence; a part starts on a tile boundary).
+  const int64_t n_chunks = (p.L + T - 1) / T;
+  const int64_t tile0 = t_begin / T;
   auto store_chunk_state = [&](int64_t tile) {
-    if (p.chunk_states == nullptr) return;
-    float* cb = p.chunk_states + ((static_cast<int64_t>(b) * n_chunks + tile) * nd + cg * 16) * N;
+    if (FOLD || p.chunk_states == nullptr) return;
+    float* cb = p.chunk_states + ((static_cast<int64_t>(b) * n_chunks + tile0 + tile) * nd + cg * 16) * N;
 #pragma unroll
     for (int k = 0; k < PPL; ++k)
       if (pair_valid(k)) cb[pair_offset(k)] = carry[k];
@@ -329,13 +377,16 @@ __global__ __launch_bounds__(64 * W, kMinWavesPerSimd<G>) void ssm_fwd_kernel(Fw
   // byte offsets of its first step in a tile.
   const int64_t xd_step = static_cast<int64_t>(nd) * E;  // bytes between consecutive steps of x/delta/y
   const int64_t bc_step = static_cast<int64_t>(N) * E;   // ... of B/C
+  // The part's rows start at b * (whole row) + t_begin * step and span L steps.
+  const int64_t xd_base = (b * p.L + t_begin) * xd_step, bc_base = (b * p.L + t_begin) * bc_step;
   const int64_t xd_row = L * xd_step, bc_row = L * bc_step;
-  const rsrc_t rx = make_rsrc(static_cast<const char*>(p.x) + b * xd_row, xd_row);
-  const rsrc_t rd = make_rsrc(static_cast<const char*>(p.delta) + b * xd_row, xd_row);
-  const rsrc_t ry = make_rsrc(static_cast<char*>(p.y) + b * xd_row, xd_row);
-  const rsrc_t rb = make_rsrc(static_cast<const char*>(p.B) + b * bc_row, bc_row);
-  const rsrc_t rc = make_rsrc(static_cast<const char*>(p.C) + b * bc_row, bc_row);
-  const rsrc_t rz = make_rsrc(GATE ? static_cast<const char*>(p.z) + b * xd_row : nullptr, GATE ? xd_row : 0);
+  const rsrc_t rx = make_rsrc(static_cast<const char*>(p.x) + xd_base, xd_row);
+  const rsrc_t rd = make_rsrc(static_cast<const char*>(p.delta) + xd_base, xd_row);
+  const rsrc_t ry = make_rsrc(FOLD ? nullptr : static_cast<char*>(p.y) + xd_base, FOLD ? 0 : xd_row);
+  const rsrc_t rb = make_rsrc(static_cast<const char*>(p.B) + bc_base, bc_row);
+  const rsrc_t rc = make_rsrc(FOLD ? nullptr : static_cast<const char*>(p.C) + bc_base, FOLD ? 0 : bc_row);
+  const rsrc_t rz = make_rsrc(GATE && !FOLD ? static_cast<const char*>(p.z) + xd_base : nullptr,
+                              GATE && !FOLD ? xd_row : 0);
   const uint32_t off_xd = static_cast<uint32_t>((j * K * nd + d) * E);
   const uint32_t off_bc = static_cast<uint32_t>((j * K * N + 16 * g + c) * E);
 
@@ -366,7 +417,7 @@ __global__ __launch_bounds__(64 * W, kMinWavesPerSimd<G>) void ssm_fwd_kernel(Fw
       const bool ok = FULL || i < left;
       const uint32_t sb = static_cast<uint32_t>((t_tile + i) * bc_step);
       bv[i] = ok ? Elem<IO>::template load<0>(rb, off_bc, sb) : 0.0f;
-      cv[i] = ok ? Elem<IO>::template load<0>(rc, off_bc, sb) : 0.0f;
+      cv[i] = (ok && !FOLD) ? Elem<IO>::template load<0>(rc, off_bc, sb) : 0.0f;
     }
     if (prefetch) load_xd.template operator()<true>(t_tile + T, nxv, ndv);
     float A2[16];
@@ -448,16 +499,20 @@ __global__ __launch_bounds__(64 * W, kMinWavesPerSimd<G>) void ssm_fwd_kernel(Fw
 #pragma unroll
           for (int u = 0; u < WB; ++u) bb[u] = pbw[(j0 + u) * (N / 4) * 64];
 #pragma unroll
-          for (int u = 0; u < WB; ++u) av[u] = fast_exp2(a2 * av[u]);
+          for (int u = 0; u < WB; ++u) {
+            if constexpr (FOLD) part_sd[k] += av[u];
+            av[u] = fast_exp2(a2 * av[u]);
+          }
 #pragma unroll
           for (int u = 0; u < WB; ++u) {
-            pbw[(j0 + u) * (N / 4) * 64] = cr;
+            if constexpr (!FOLD) pbw[(j0 + u) * (N / 4) * 64] = cr;
             cr = __builtin_fmaf(av[u], cr, bb[u]);
           }
         }
         carry[k] = cr;
       }
     }
+    if constexpr (FOLD) return;  // the next tile's pass 1 writes the other record buffer
     store_chunk_state(t_tile / T);
     __syncthreads();
 
@@ -520,22 +575,36 @@ __global__ __launch_bounds__(64 * W, kMinWavesPerSimd<G>) void ssm_fwd_kernel(Fw
     tile_body.template operator()<false>(t_next, static_cast<int>(nfull & 1), xa, da, false, xn, dn);
     t_next += T;
   }
-  // Tiles wholly in the padding: the carry is unchanged and y is +0.
-  for (; t_next < L; t_next += T) {
-    store_chunk_state(t_next / T);
-    const int64_t left = L - t_next - j * K;
+  if constexpr (FOLD) {
+    // Part 0 leaves the state entering part 1; a later part its b_total
+    // (folded from zero) and the delta sum of each channel over its valid steps.
+    float* wb = p.ws + part * ws_block + state_block;
 #pragma unroll
-    for (int i = 0; i < K; ++i) {
-      if (i < left && (G == 1 || (i % G) == g))
-        Elem<IO>::store(ry, off_xd, static_cast<uint32_t>((t_next + i) * xd_step), 0.0f);
+    for (int k = 0; k < PPL; ++k) {
+      if (pair_valid(k)) {
+        wb[pair_offset(k)] = carry[k];
+        int cc, n;
+        pair_of(k, cc, n);
+        if (part > 0 && n == 0) ws_sd[(static_cast<int64_t>(part - 1) * p.nb + b) * nd + cg * 16 + cc] = part_sd[k];
+      }
     }
-  }
-
-  if (p.h_last != nullptr) {
-    float* hb = p.h_last + state_block;
+  } else {
+    // Tiles wholly in the padding: the carry is unchanged and y is +0.
+    for (; t_next < L; t_next += T) {
+      store_chunk_state(t_next / T);
+      const int64_t left = L - t_next - j * K;
 #pragma unroll
-    for (int k = 0; k < PPL; ++k)
-      if (pair_valid(k)) hb[pair_offset(k)] = carry[k];
+      for (int i = 0; i < K; ++i) {
+        if (i < left && (G == 1 || (i % G) == g))
+          Elem<IO>::store(ry, off_xd, static_cast<uint32_t>((t_next + i) * xd_step), 0.0f);
+      }
+    }
+    if (p.h_last != nullptr && part == p.n_parts - 1) {
+      float* hb = p.h_last + state_block;
+#pragma unroll
+      for (int k = 0; k < PPL; ++k)
+        if (pair_valid(k)) hb[pair_offset(k)] = carry[k];
+    }
   }
 }
 
@@ -562,9 +631,18 @@ struct Config<IO, 4> {
 template <typename IO, int G, bool SP, bool CL, bool GATE>
 hipError_t launch_flags(const FwdParams& prm, hipStream_t stream) {
   constexpr int K = Config<IO, G>::K, W = Config<IO, G>::W;
-  const int64_t blocks = static_cast<int64_t>(prm.nb) * prm.n_cg;
-  hipLaunchKernelGGL((ssm_fwd_kernel<IO, G, K, W, SP, CL, GATE>), dim3(static_cast<unsigned>(blocks)), dim3(64 * W),
-                     0, stream, prm);
+  const int64_t groups = static_cast<int64_t>(prm.nb) * prm.n_cg;
+  if (prm.n_parts > 1) {
+    // The fold of parts 0 .. n_parts-2 must be complete before any part reads
+    // its incoming state: same stream, launched first.  The fold never loads
+    // z, so it has no gate variant.
+    hipLaunchKernelGGL((ssm_fwd_kernel<IO, G, K, W, SP, CL, false, true>),
+                       dim3(static_cast<unsigned>(groups * (prm.n_parts - 1))), dim3(64 * W), 0, stream, prm);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((ssm_fwd_kernel<IO, G, K, W, SP, CL, GATE, false>),
+                     dim3(static_cast<unsigned>(groups * prm.n_parts)), dim3(64 * W), 0, stream, prm);
   return hipGetLastError();
 }
 
@@ -618,6 +696,28 @@ __global__ void copy_fill_kernel(float* dst, const float* src, int64_t n) {
   if (i < n) dst[i] = (src != nullptr) ? src[i] : 0.0f;
 }
 
+// Geometry of a time split into (at most) `parts` parts: whole tiles per part.
+struct Split {
+  int64_t parts;     // parts actually used (>= 1)
+  int64_t part_len;  // steps per part (the last may be shorter)
+};
+
+Split split_for(int64_t L, int64_t N, int64_t parts) {
+  const int64_t T = tile_steps(N);
+  const int64_t n_tiles = L > 0 ? (L + T - 1) / T : 0;
+  if (parts <= 1 || n_tiles <= 1) return {1, L};
+  const int64_t per = (n_tiles + parts - 1) / parts;
+  return {(n_tiles + per - 1) / per, per * T};
+}
+
+// Workspace floats of a split: the states entering parts 1 .. P-1 (the first
+// directly, the others as b_total of the part before) and the delta sums of
+// parts 1 .. P-2.
+int64_t split_ws_floats(const Split& sp, int64_t nb, int64_t nd, int64_t N) {
+  if (sp.parts <= 1) return 0;
+  return (sp.parts - 1) * nb * nd * N + (sp.parts > 2 ? (sp.parts - 2) * nb * nd : 0);
+}
+
 bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
   const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
@@ -632,6 +732,26 @@ struct ssm_scan_handle_s {
   int device;
   int cu_count;
 };
+
+namespace {
+
+// Parts for an automatic time split: none while the (row, channel group)
+// workgroups alone fill the GPU; otherwise enough parts that the fold of the
+// first P-1 parts and the parts themselves each occupy every CU, at most 8
+// and at least four tiles per part.
+int64_t auto_parts(const ssm_scan_handle_s* h, int64_t nb, int64_t L, int64_t nd, int64_t N) {
+  if (N != 16 && N != 32 && N != 64) return 1;
+  const int64_t groups = nb * (nd / 16);
+  const int64_t slots = static_cast<int64_t>(h->cu_count) * (N == 16 ? 2 : 1);  // resident workgroups
+  if (groups <= 0 || groups >= slots) return 1;
+  int64_t parts = (2 * slots + groups - 1) / groups;
+  if (parts > 8) parts = 8;
+  const int64_t max_by_len = L / (4 * tile_steps(N));
+  if (parts > max_by_len) parts = max_by_len;
+  return parts < 1 ? 1 : split_for(L, N, parts).parts;
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -686,6 +806,18 @@ const char* ssm_scan_error_string(int code) {
 
 int64_t ssm_scan_chunk_len(int64_t dstate) { return tile_steps(dstate); }
 
+int32_t ssm_scan_auto_time_parts(ssm_scan_t handle, const ssm_scan_dims* dims) {
+  if (handle == nullptr || dims == nullptr || dims->batch < 0 || dims->seqlen < 0 || dims->dim < 0) return 1;
+  return static_cast<int32_t>(auto_parts(handle, dims->batch, dims->seqlen, dims->dim, dims->dstate));
+}
+
+int64_t ssm_scan_workspace_bytes(const ssm_scan_dims* dims, int32_t time_parts) {
+  if (dims == nullptr || time_parts < 0 || dims->batch < 0 || dims->seqlen < 0 || dims->dim < 0) return -1;
+  if (tile_steps(dims->dstate) == 0) return -1;
+  const Split sp = split_for(dims->seqlen, dims->dstate, time_parts);
+  return 4 * split_ws_floats(sp, dims->batch, dims->dim, dims->dstate);
+}
+
 // Checks run in this order: dims, sizes and flags; pointers; alignment;
 // aliasing; the handle; the current device.  Nothing is enqueued unless all
 // pass.
@@ -712,9 +844,17 @@ int ssm_selective_scan_fwd_ex(ssm_scan_t handle, const void* x, const void* delt
   const int64_t esz = dims->io_dtype == SSM_IO_BF16 ? 2 : 4;
   if (L > 0 && L * (N > nd ? N : nd) * esz > 0x7fffffffLL) return SSM_ERR_UNSUPPORTED;
 
-  const ssm_scan_fwd_extras none = {nullptr, nullptr, nullptr, nullptr, 0};
+  const ssm_scan_fwd_extras none = {nullptr, nullptr, nullptr, nullptr, 0, 0, nullptr, 0};
   const ssm_scan_fwd_extras& ex = extras ? *extras : none;
   if (ex.chunk_states != nullptr && ex.chunk_len != tile_steps(N)) return SSM_ERR_INVALID_ARG;
+  if (ex.time_parts < 0 || ex.workspace_bytes < 0 || (ex.workspace == nullptr && ex.workspace_bytes != 0))
+    return SSM_ERR_INVALID_ARG;
+  // An explicit split needs its workspace; the automatic one is skipped when
+  // the workspace is missing or too small.
+  if (ex.time_parts >= 2) {
+    const Split sp = split_for(L, N, ex.time_parts);
+    if (4 * split_ws_floats(sp, nb, nd, N) > ex.workspace_bytes) return SSM_ERR_INVALID_ARG;
+  }
 
   const bool empty = (nb == 0 || nd == 0);
   const size_t e = static_cast<size_t>(esz);
@@ -727,7 +867,8 @@ int ssm_selective_scan_fwd_ex(ssm_scan_t handle, const void* x, const void* delt
       return SSM_ERR_INVALID_ARG;
     if (!aligned(x, e) || !aligned(delta, e) || !aligned(B, e) || !aligned(C, e) || !aligned(y, e) ||
         !aligned(ex.z, e) || !aligned(A_log, 4) || !aligned(D, 4) || !aligned(valid_len, 4) || !aligned(h_last, 4) ||
-        !aligned(ex.h0, 4) || !aligned(ex.delta_bias, 4) || !aligned(ex.chunk_states, 4))
+        !aligned(ex.h0, 4) || !aligned(ex.delta_bias, 4) || !aligned(ex.chunk_states, 4) ||
+        !aligned(ex.workspace, 4))
       return SSM_ERR_UNSUPPORTED;
     const size_t by = L > 0 ? n_xd * e : 0, bh = h_last ? n_state * 4 : 0;
     const size_t bcs = ex.chunk_states ? n_chunks * n_state * 4 : 0;
@@ -745,6 +886,13 @@ int ssm_selective_scan_fwd_ex(ssm_scan_t handle, const void* x, const void* delt
     }
     if (overlaps(y, by, h_last, bh) || overlaps(y, by, ex.chunk_states, bcs) ||
         overlaps(h_last, bh, ex.chunk_states, bcs))
+      return SSM_ERR_ALIAS;
+    // The workspace is written by the library: it may overlap nothing else.
+    const size_t bw = static_cast<size_t>(ex.workspace_bytes);
+    for (int k = 0; k < 10; ++k)
+      if (overlaps(ex.workspace, bw, ins[k], ins_n[k])) return SSM_ERR_ALIAS;
+    if (overlaps(ex.workspace, bw, y, by) || overlaps(ex.workspace, bw, h_last, bh) ||
+        overlaps(ex.workspace, bw, ex.chunk_states, bcs))
       return SSM_ERR_ALIAS;
   }
   if (handle == nullptr) return SSM_ERR_INVALID_ARG;
@@ -794,6 +942,16 @@ int ssm_selective_scan_fwd_ex(ssm_scan_t handle, const void* x, const void* delt
   prm.clamp = dims->delta_clamp;
   prm.dmin = dims->delta_min;
   prm.dmax = dims->delta_max;
+  int64_t parts = ex.time_parts;
+  if (parts == 0) {
+    parts = auto_parts(handle, nb, L, nd, N);
+    if (parts >= 2 && 4 * split_ws_floats(split_for(L, N, parts), nb, nd, N) > ex.workspace_bytes) parts = 1;
+  }
+  const Split sp = split_for(L, N, parts);
+  if (static_cast<int64_t>(nb) * (nd / 16) * sp.parts > 0x7fffffffLL) return SSM_ERR_UNSUPPORTED;
+  prm.ws = static_cast<float*>(ex.workspace);
+  prm.part_len = sp.part_len;
+  prm.n_parts = static_cast<int32_t>(sp.parts);
   const int G = static_cast<int>(N / 16);
   const hipError_t err =
       dims->io_dtype == SSM_IO_BF16 ? launch_io<uint16_t>(G, prm, s) : launch_io<float>(G, prm, s);

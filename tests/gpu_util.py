@@ -19,11 +19,14 @@ def to_device(inp: dict, io: str, device="cuda:0"):
     return out
 
 
-def run_gpu(dev: dict, delta_softplus=True, delta_clamp=None, sync=True):
+def run_gpu(dev: dict, delta_softplus=True, delta_clamp=None, sync=True, time_parts=None):
+    """The forward through the binding; time_parts None lets the library choose
+    its time split (the product default), 1 disables it."""
     import torch
     import selective_state_space_scan_amd as ssm
     y, h = ssm.selective_scan_fwd(dev["x"], dev["delta"], dev["A_log"], dev["B"], dev["C"], dev["D"],
-                                  dev["valid_len"], delta_softplus=delta_softplus, delta_clamp=delta_clamp)
+                                  dev["valid_len"], delta_softplus=delta_softplus, delta_clamp=delta_clamp,
+                                  time_parts=time_parts)
     if sync:
         torch.cuda.synchronize()
     return y, h

@@ -128,6 +128,36 @@ def test_extras_checks():
     assert _ex_call(_dims(), E(chunk_states=PTRS["h_last"], chunk_len=128)) == ssm.SSM_ERR_ALIAS
 
 
+def test_time_split_checks():
+    E = ssm.ssm_scan_fwd_extras
+    d = _dims(batch=2, seqlen=1000, dim=32, dstate=16)
+    # 8 tiles of 128 steps; 3 parts of 3, 3 and 2 tiles: two state blocks and one delta-sum block
+    assert ssm.workspace_bytes(d, 3) == 4 * (2 * 2 * 32 * 16 + 2 * 32)
+    assert ssm.workspace_bytes(d, 2) == 4 * (2 * 32 * 16)
+    assert ssm.workspace_bytes(d, 1) == 0 and ssm.workspace_bytes(d, 0) == 0
+    assert ssm.workspace_bytes(d, 100) == 4 * (7 * 2 * 32 * 16 + 6 * 2 * 32)  # at most one part per tile
+    assert ssm.workspace_bytes(d, -1) == -1 and ssm.workspace_bytes(_dims(dstate=8), 2) == -1
+    assert ssm.workspace_bytes(_dims(seqlen=100, dstate=16), 4) == 0  # one tile: no split
+    assert ssm.auto_time_parts(None, d) == 1
+    need = ssm.workspace_bytes(d, 3)
+    bad_x = dict(x=PTRS["x"] + 1)  # a misaligned input: fails after the extras checks
+    # an explicit split with too small (or no) workspace is rejected before anything else
+    assert _ex_call(d, E(time_parts=3, workspace=8 * MB, workspace_bytes=need - 4), **bad_x) == ssm.SSM_ERR_INVALID_ARG
+    assert _ex_call(d, E(time_parts=3), **bad_x) == ssm.SSM_ERR_INVALID_ARG
+    assert _ex_call(d, E(time_parts=3, workspace=8 * MB, workspace_bytes=need), **bad_x) == ssm.SSM_ERR_UNSUPPORTED
+    assert _ex_call(d, E(time_parts=-1), **bad_x) == ssm.SSM_ERR_INVALID_ARG
+    assert _ex_call(d, E(workspace_bytes=64), **bad_x) == ssm.SSM_ERR_INVALID_ARG  # bytes without a pointer
+    # automatic and no split never need a workspace
+    assert _ex_call(d, E(time_parts=0), **bad_x) == ssm.SSM_ERR_UNSUPPORTED
+    assert _ex_call(d, E(time_parts=1), **bad_x) == ssm.SSM_ERR_UNSUPPORTED
+    # the workspace must be aligned and overlap nothing
+    assert _ex_call(d, E(time_parts=3, workspace=8 * MB + 2, workspace_bytes=need)) == ssm.SSM_ERR_UNSUPPORTED
+    assert _ex_call(d, E(time_parts=3, workspace=PTRS["B"], workspace_bytes=need)) == ssm.SSM_ERR_ALIAS
+    assert _ex_call(d, E(time_parts=3, workspace=PTRS["y"] - 64, workspace_bytes=need)) == ssm.SSM_ERR_ALIAS
+    assert _ex_call(d, E(time_parts=3, workspace=PTRS["h_last"], workspace_bytes=need)) == ssm.SSM_ERR_ALIAS
+    assert _ex_call(d, E(time_parts=3, workspace=8 * MB, workspace_bytes=need)) == ssm.SSM_ERR_INVALID_ARG  # handle
+
+
 def test_empty_problem_needs_only_the_handle():
     assert call(_dims(batch=0), x=None, delta=None, B=None, C=None, y=None, A_log=None) == ssm.SSM_ERR_INVALID_ARG
 

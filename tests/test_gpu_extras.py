@@ -88,18 +88,21 @@ def test_chunk_states_against_oracle(io, N):
 def test_split_at_chunk_boundary_is_bitwise(N):
     """bjdmk.com.cn section 2.4 / pwwt.cn section 4.2: carrying the state into a
     second run continues the sequence.  Split at a multiple of the chunk
-    length, the two runs take exactly the same arithmetic as one run."""
+    length, the two runs take exactly the same arithmetic as one run (all
+    three without the library's own time split)."""
     import torch
     import selective_state_space_scan_amd as ssm
     w, inp = _case("bf16", N, L=1000, seed=3 * N)
     dev = to_device(inp, "bf16")
-    y, h = ssm.selective_scan_fwd(dev["x"], dev["delta"], dev["A_log"], dev["B"], dev["C"], dev["D"], None)
+    y, h = ssm.selective_scan_fwd(dev["x"], dev["delta"], dev["A_log"], dev["B"], dev["C"], dev["D"], None,
+                                  time_parts=1)
     T = 3 * ssm.chunk_len(N)
     part = lambda t, a, b: t[:, a:b].contiguous()
     y1, h1 = ssm.selective_scan_fwd(part(dev["x"], 0, T), part(dev["delta"], 0, T), dev["A_log"],
-                                    part(dev["B"], 0, T), part(dev["C"], 0, T), dev["D"], None)
+                                    part(dev["B"], 0, T), part(dev["C"], 0, T), dev["D"], None, time_parts=1)
     y2, h2 = ssm.selective_scan_fwd(part(dev["x"], T, 1000), part(dev["delta"], T, 1000), dev["A_log"],
-                                    part(dev["B"], T, 1000), part(dev["C"], T, 1000), dev["D"], None, h0=h1)
+                                    part(dev["B"], T, 1000), part(dev["C"], T, 1000), dev["D"], None, h0=h1,
+                                    time_parts=1)
     torch.cuda.synchronize()
     assert np.array_equal(_bits(torch.cat([y1, y2], dim=1)), _bits(y))
     assert np.array_equal(_bits(h2), _bits(h))

@@ -20,12 +20,16 @@ LENGTHS = [0, 1, 3, 4, 5, 63, 64, 65, 127, 128, 129, 255, 256, 257, 600, 999, 10
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
 @pytest.mark.parametrize("N", [16, 64])
-def test_padding_bit_exact(io, N):
+@pytest.mark.parametrize("parts", [1, None])
+def test_padding_bit_exact(io, N, parts):
     """pwwt.cn section 2.3 / 5.2: padding is the identity and must not touch
     the valid outputs.  y at padded steps is +0.0; garbage (NaN, Inf) in the
-    padding changes nothing; valid_len = L matches no valid_len; a padded row
-    equals the same row run alone with its own length (bitwise)."""
+    padding changes nothing; valid_len = L matches no valid_len; without a time
+    split, a padded row equals the same row run alone with its own length
+    (bitwise).  parts None: the library's own time split (7 parts at N = 64)."""
+    import functools
     import torch
+    run = functools.partial(run_gpu, time_parts=parts)
     L = 1000
     base = I.WORKLOADS[0] if io == "f32" else I.WORKLOADS[3]
     w = I.small_workload(base, batch=len(LENGTHS), seqlen=L, dim=32)
@@ -33,7 +37,7 @@ def test_padding_bit_exact(io, N):
     inp = I.make_inputs(w, 31337 + N)
     inp["valid_len"] = np.array(LENGTHS, np.int32)
     dev = to_device(inp, io)
-    y, h = run_gpu(dev)
+    y, h = run(dev)
     yb, hb = _bits(y), _bits(h)
     for b, l in enumerate(LENGTHS):
         assert np.all(yb[b, l:] == 0), f"row {b}: padded y must be +0.0 bits"
@@ -44,27 +48,29 @@ def test_padding_bit_exact(io, N):
         garb["delta"][b, l:] = float("inf")
         garb["B"][b, l:] = float("nan")
         garb["C"][b, l:] = float("-inf")
-    y2, h2 = run_gpu(dict(dev, **garb))
+    y2, h2 = run(dict(dev, **garb))
     assert np.array_equal(_bits(y2), yb) and np.array_equal(_bits(h2), hb)
-    # each row alone, truncated to its length
+    # each row alone, truncated to its length (a split depends on the length)
     for b, l in enumerate(LENGTHS):
         if l == 0:
             assert np.all(to_np64(h[b]) == 0.0)
             continue
+        if parts != 1:
+            continue
         one = {k: dev[k][b:b + 1, :l].contiguous() for k in ("x", "delta", "B", "C")}
         one.update(A_log=dev["A_log"], D=dev["D"], valid_len=None)
-        y1, h1 = run_gpu(one)
+        y1, h1 = run(one)
         assert np.array_equal(_bits(y1)[0], yb[b, :l]), f"row {b} (len {l}): y differs from the row run alone"
         assert np.array_equal(_bits(h1)[0], hb[b]), f"row {b} (len {l}): h_last differs"
     # valid_len all = L vs none; and out-of-range lengths clamp
     full = dict(dev, valid_len=torch.full((w.batch,), L, dtype=torch.int32, device=y.device))
     over = dict(dev, valid_len=torch.full((w.batch,), L + 7, dtype=torch.int32, device=y.device))
     none = dict(dev, valid_len=None)
-    r_full, r_over, r_none = run_gpu(full), run_gpu(over), run_gpu(none)
+    r_full, r_over, r_none = run(full), run(over), run(none)
     assert np.array_equal(_bits(r_full[0]), _bits(r_none[0])) and np.array_equal(_bits(r_full[1]), _bits(r_none[1]))
     assert np.array_equal(_bits(r_over[0]), _bits(r_none[0])) and np.array_equal(_bits(r_over[1]), _bits(r_none[1]))
     neg = dict(dev, valid_len=torch.full((w.batch,), -5, dtype=torch.int32, device=y.device))
-    yn, hn = run_gpu(neg)
+    yn, hn = run(neg)
     assert np.all(_bits(yn) == 0) and np.all(_bits(hn) == 0)
 
 
@@ -74,12 +80,12 @@ def test_config3_lengths_bit_exact_rows():
     w = I.small_workload(I.WORKLOADS[3], batch=6, seqlen=8192, dim=16)
     inp = I.make_inputs(w, I.seed_for(3) + 7)
     dev = to_device(inp, w.io)
-    y, h = run_gpu(dev)
+    y, h = run_gpu(dev, time_parts=1)
     for b in range(w.batch):
         l = int(inp["valid_len"][b])
         one = {k: dev[k][b:b + 1, :l].contiguous() for k in ("x", "delta", "B", "C")}
         one.update(A_log=dev["A_log"], D=dev["D"], valid_len=None)
-        y1, h1 = run_gpu(one)
+        y1, h1 = run_gpu(one, time_parts=1)
         assert np.array_equal(_bits(y1)[0], _bits(y)[b, :l]) and np.array_equal(_bits(h1)[0], _bits(h)[b])
         assert np.all(_bits(y)[b, l:] == 0)
 
