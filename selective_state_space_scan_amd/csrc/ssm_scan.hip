@@ -226,10 +226,10 @@ struct Unroll<K, K> {
 
 // ---- the kernel ----------------------------------------------------------
 
-// dstate 16 fits 128 VGPRs, so two 8-wave workgroups share a CU (4 waves per
-// SIMD); wider states keep 2 waves per SIMD rather than spill.
-template <int G>
-constexpr int kMinWavesPerSimd = (G == 1) ? 4 : 2;
+// 128 VGPRs, so that two 8-wave workgroups share a CU (4 waves per SIMD).
+// dstate 32 and 64 spill a few registers per tile to get there (measured: the
+// second workgroup per CU is worth far more than the spills cost).
+constexpr int kMinWavesPerSimd = 4;
 
 // FOLD: the fold kernel of the time split -- pass 1 and the carry walk only,
 // over parts 0 .. n_parts-2, leaving each part's carry-out (part 0, from h0)
@@ -237,7 +237,7 @@ constexpr int kMinWavesPerSimd = (G == 1) ? 4 : 2;
 // Otherwise the full forward over every part, each starting from the state
 // the workspace gives for its first step.
 template <typename IO, int G, int K, int W, bool SOFTPLUS, bool CLAMP, bool GATE, bool FOLD>
-__global__ __launch_bounds__(64 * W, FOLD ? 4 : kMinWavesPerSimd<G>) void ssm_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(64 * W, kMinWavesPerSimd) void ssm_fwd_kernel(FwdParams p) {
   constexpr int N = 16 * G;             // states per channel
   constexpr int QR = 4 / G;             // time sub-chunks per wave
   constexpr int SUB = W * QR;           // sub-chunks per tile
@@ -742,7 +742,7 @@ namespace {
 int64_t auto_parts(const ssm_scan_handle_s* h, int64_t nb, int64_t L, int64_t nd, int64_t N) {
   if (N != 16 && N != 32 && N != 64) return 1;
   const int64_t groups = nb * (nd / 16);
-  const int64_t slots = static_cast<int64_t>(h->cu_count) * (N == 16 ? 2 : 1);  // resident workgroups
+  const int64_t slots = static_cast<int64_t>(h->cu_count) * 2;  // resident workgroups: two per CU
   if (groups <= 0 || groups >= slots) return 1;
   int64_t parts = (2 * slots + groups - 1) / groups;
   if (parts > 8) parts = 8;

@@ -114,4 +114,4 @@ def test_headline_shape_is_not_split():
     w = I.WORKLOADS[4]
     dims = ssm.ssm_scan_dims()
     dims.batch, dims.seqlen, dims.dim, dims.dstate, dims.io_dtype = w.batch, w.seqlen, w.dim, w.dstate, 1
-    assert ssm.auto_time_parts(h, dims) == 4
+    assert ssm.auto_time_parts(h, dims) == 8
