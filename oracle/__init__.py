@@ -72,6 +72,8 @@ def _load(mutation: int = 0) -> ctypes.CDLL:
         lib.oracle_selective_scan_ex.restype = ctypes.c_int
         lib.oracle_selective_scan_rows.argtypes = common + [d, d, i64p, i64p, i64, d, d, ctypes.c_int]
         lib.oracle_selective_scan_rows.restype = ctypes.c_int
+        lib.oracle_selective_scan_bwd.argtypes = common + [d, d, d, d] + [d] * 9 + [ctypes.c_int]
+        lib.oracle_selective_scan_bwd.restype = ctypes.c_int
         lib.oracle_mutation_id.argtypes = []
         lib.oracle_mutation_id.restype = ctypes.c_int
         _libs[mutation] = lib
@@ -193,3 +195,35 @@ def selective_scan_rows(x, delta, A_log, B, C, rows, D=None, valid_len=None, h0=
     if rc != 0:
         raise RuntimeError(f"oracle_selective_scan_rows failed ({rc})")
     return y, h
+
+
+def selective_scan_bwd(x, delta, A_log, B, C, D=None, dy=None, valid_len=None, h0=None, delta_softplus: bool = True,
+                       delta_clamp=None, delta_bias=None, z=None, dh_last=None, nthreads: int = 1,
+                       mutation: int = 0) -> dict:
+    """Gradients of the forward for the loss sum(dy * y) + sum(dh_last * h_last)
+    (reverse-mode differentiation of the serial loop; see ssm_oracle.c).
+    Returns a dict of fp64 arrays: dx, ddelta (w.r.t. the raw delta), dA_log,
+    dB, dC, dD, ddelta_bias, dz (None without z), dh0."""
+    x, delta, A_log, B, C, D, vl, h0, nb, L, nd, N = _prep(x, delta, A_log, B, C, D, valid_len, h0)
+    delta_bias, z = _extras(delta_bias, z, nb, L, nd)
+    dy = _f64(dy)
+    if dy is None or dy.shape != (nb, L, nd):
+        raise ValueError("dy must be [B, L, D]")
+    dh_last = _f64(dh_last)
+    if dh_last is not None and dh_last.shape != (nb, nd, N):
+        raise ValueError("dh_last must be [B, D, N]")
+    clamp = delta_clamp is not None
+    dmin, dmax = (float(delta_clamp[0]), float(delta_clamp[1])) if clamp else (0.0, 0.0)
+    out = dict(dx=np.empty((nb, L, nd)), ddelta=np.empty((nb, L, nd)), dA_log=np.empty((nd, N)),
+               dB=np.empty((nb, L, N)), dC=np.empty((nb, L, N)), dD=np.empty(nd), ddelta_bias=np.empty(nd),
+               dz=np.empty((nb, L, nd)) if z is not None else None, dh0=np.empty((nb, nd, N)))
+    rc = _load(mutation).oracle_selective_scan_bwd(
+        _ptr(x), _ptr(delta), _ptr(A_log), _ptr(B), _ptr(C), _ptr(D), _ptr(vl, ctypes.c_int32), _ptr(h0),
+        nb, L, nd, N, int(bool(delta_softplus)), int(clamp), dmin, dmax, _ptr(delta_bias), _ptr(z), _ptr(dy),
+        _ptr(dh_last), _ptr(out["dx"]), _ptr(out["ddelta"]), _ptr(out["dA_log"]), _ptr(out["dB"]), _ptr(out["dC"]),
+        _ptr(out["dD"]), _ptr(out["ddelta_bias"]), _ptr(out["dz"]), _ptr(out["dh0"]), int(nthreads))
+    if rc != 0:
+        raise RuntimeError(f"oracle_selective_scan_bwd failed ({rc})")
+    if D is None:
+        out["dD"] = None
+    return out

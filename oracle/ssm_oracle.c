@@ -341,4 +341,233 @@ ORACLE_API int oracle_selective_scan_rows(const double* x, const double* delta, 
   return run_job(&job, nthreads);
 }
 
+/* ---- backward --------------------------------------------------------
+ *
+ * Gradients of the forward above by reverse-mode differentiation of the plain
+ * serial loop (the recomputation from saved states the pwwt.cn article,
+ * section 3.4, describes, here with the full per-step history of one row kept
+ * in memory, which the oracle can afford).  With the loss
+ *     L = sum dy * y + sum dh_last * h_last
+ * the adjoint of the state after step t is
+ *     g_t = dh_last (t = last valid step) + dypre_t * C_t + Abar_{t+1} g_{t+1},
+ * where dypre_t = dy_t * silu(z_t) with the gate (else dy_t), and per step:
+ *     dC[b,t,n] += dypre_t h_t[n]                 dB[b,t,n] += g_t[n] Delta_t x_t
+ *     dx_t = dypre_t D + sum_n g_t[n] Delta_t B_t[n]
+ *     dDelta_t = sum_n g_t[n] (B_t[n] x_t + h_{t-1}[n] Abar_t[n] A[n])
+ *     dA[n] += g_t[n] h_{t-1}[n] Abar_t[n] Delta_t,  dA_log = dA * A
+ *     dD += dypre_t x_t,   dz_t = dy_t ypre_t silu'(z_t)
+ * and dDelta_raw = dDelta * [clip inactive] * sigmoid(raw + bias) (softplus'),
+ * ddelta_bias = sum over (b, t) of dDelta_raw, dh0 = Abar_0 g_0 (the adjoint of
+ * the state before step 0).  Padded steps contribute nothing and get zero
+ * gradients.  The clip passes the gradient where dmin <= softplus <= dmax.
+ */
+
+typedef struct {
+  const problem_t* p;
+  const double* dy;      /* [nb, L, nd] */
+  const double* dh_last; /* [nb, nd, N] or NULL */
+  double *dx, *ddelta, *dB, *dC, *dz, *dh0; /* full tensors (dz, dh0 may be NULL) */
+  double *dA_part, *dD_part, *dbias_part;   /* per batch row: [nb, nd, N], [nb, nd], [nb, nd] */
+  int nthreads;
+  int status;
+} bwd_job_t;
+
+typedef struct {
+  bwd_job_t* job;
+  int k;
+} bwd_arg_t;
+
+static double sigmoid(double v) { return v >= 0.0 ? 1.0 / (1.0 + exp(-v)) : exp(v) / (1.0 + exp(v)); }
+
+/* One (b, d) row: forward with the full history, then the reverse sweep. */
+static void bwd_row(bwd_job_t* j, int64_t b, int64_t d, double* hist /* (L+1) * N */, double* abar /* L * N */,
+                    double* dlt /* L */, double* dfac /* L */, double* A /* N */, double* g /* N */) {
+  const problem_t* p = j->p;
+  const int64_t L = p->L, N = p->N, nd = p->nd;
+  int64_t len = L;
+  if (p->valid_len) {
+    int64_t v = p->valid_len[b];
+    len = v < 0 ? 0 : (v > L ? L : v);
+  }
+  for (int64_t n = 0; n < N; ++n) {
+    A[n] = -exp(p->A_log[d * N + n]);
+    hist[n] = p->h0 ? p->h0[(b * nd + d) * N + n] : 0.0;
+  }
+  /* forward: hist[(t + 1) * N + n] = h_t[n] */
+  for (int64_t t = 0; t < len; ++t) {
+    const int64_t i = (b * L + t) * nd + d;
+    double raw = p->delta[i];
+    if (p->delta_bias) raw += p->delta_bias[d];
+    double dt = p->softplus ? oracle_softplus(raw) : raw;
+    double fac = p->softplus ? sigmoid(raw) : 1.0;
+#if ORACLE_MUTATION == 13
+    fac = 1.0; /* planted: softplus derivative missing */
+#endif
+    if (p->clamp) {
+      if (dt < p->dmin || dt > p->dmax) fac = 0.0;
+      if (dt < p->dmin) dt = p->dmin;
+      if (dt > p->dmax) dt = p->dmax;
+    }
+    dlt[t] = dt;
+    dfac[t] = fac;
+    const double xt = p->x[i];
+    const double* Bt = p->B + (b * L + t) * N;
+    for (int64_t n = 0; n < N; ++n) {
+      const double a = exp(dt * A[n]);
+      abar[t * N + n] = a;
+      hist[(t + 1) * N + n] = a * hist[t * N + n] + dt * Bt[n] * xt;
+    }
+  }
+  /* reverse */
+  for (int64_t n = 0; n < N; ++n) g[n] = j->dh_last ? j->dh_last[(b * nd + d) * N + n] : 0.0;
+  const double dskip = p->D ? p->D[d] : 0.0;
+  double dD = 0.0, dbias = 0.0;
+  for (int64_t t = L - 1; t >= 0; --t) {
+    const int64_t i = (b * L + t) * nd + d;
+    if (t >= len) {
+      j->dx[i] = 0.0;
+      j->ddelta[i] = 0.0;
+      if (j->dz) j->dz[i] = 0.0;
+      continue;
+    }
+    const double xt = p->x[i], dt = dlt[t];
+    const double* Bt = p->B + (b * L + t) * N;
+    const double* Ct = p->C + (b * L + t) * N;
+    const double* ht = hist + (t + 1) * N;
+    const double* hp = hist + t * N;
+    double dyp = j->dy[i];
+    if (p->z) {
+      const double zt = p->z[i], sg = sigmoid(zt);
+      double ypre = dskip * xt;
+      for (int64_t n = 0; n < N; ++n) ypre += Ct[n] * ht[n];
+      j->dz[i] = j->dy[i] * ypre * sg * (1.0 + zt * (1.0 - sg));
+      dyp = j->dy[i] * zt * sg;
+    }
+    double dx = dyp * dskip, ddt = 0.0;
+    dD += dyp * xt;
+    for (int64_t n = 0; n < N; ++n) {
+      g[n] += dyp * Ct[n];
+      j->dC[(b * L + t) * N + n] += dyp * ht[n];
+      const double a = abar[t * N + n];
+      const double da = g[n] * hp[n];
+      ddt += g[n] * Bt[n] * xt + da * a * A[n];
+      dx += g[n] * dt * Bt[n];
+      j->dB[(b * L + t) * N + n] += g[n] * dt * xt;
+#if ORACLE_MUTATION == 12
+      j->dA_part[(b * nd + d) * N + n] += da * a; /* planted: dA without the Delta factor */
+#else
+      j->dA_part[(b * nd + d) * N + n] += da * a * dt;
+#endif
+#if ORACLE_MUTATION != 11
+      g[n] *= a;
+#endif
+      /* (mutation 11 plants an adjoint that is not decayed through the step) */
+    }
+    j->dx[i] = dx;
+    const double draw = ddt * dfac[t];
+    j->ddelta[i] = draw;
+    dbias += draw;
+  }
+  if (j->dh0)
+    for (int64_t n = 0; n < N; ++n) j->dh0[(b * nd + d) * N + n] = g[n];
+  for (int64_t n = 0; n < N; ++n) j->dA_part[(b * nd + d) * N + n] *= A[n];
+  j->dD_part[b * nd + d] = dD;
+  j->dbias_part[b * nd + d] = dbias;
+}
+
+static void* bwd_worker(void* argp) {
+  bwd_arg_t* wa = (bwd_arg_t*)argp;
+  bwd_job_t* j = wa->job;
+  const problem_t* p = j->p;
+  const int64_t L = p->L, N = p->N;
+  double* buf = (double*)malloc(sizeof(double) * (size_t)((L + 1) * N + L * N + 2 * L + 2 * N + 4));
+  if (!buf) {
+    j->status = -1;
+    return NULL;
+  }
+  double* hist = buf;
+  double* abar = hist + (L + 1) * N;
+  double* dlt = abar + L * N;
+  double* dfac = dlt + L;
+  double* A = dfac + L;
+  double* g = A + N;
+  /* batch rows are dealt to workers; one worker owns every channel of its
+   * rows, so the sums over channels (dB, dC) need no cross-thread reduction */
+  for (int64_t b = wa->k; b < p->nb; b += j->nthreads)
+    for (int64_t d = 0; d < p->nd; ++d) bwd_row(j, b, d, hist, abar, dlt, dfac, A, g);
+  free(buf);
+  return NULL;
+}
+
+/* Backward of oracle_selective_scan_ex (same inputs and flags) for the loss
+ * sum dy*y + sum dh_last*h_last.  Outputs (all fp64, overwritten):
+ * dx, ddelta (w.r.t. the raw delta) [nb, L, nd]; dA_log [nd, N]; dB, dC
+ * [nb, L, N]; dD [nd] (may be NULL); ddelta_bias [nd] (may be NULL); dz
+ * [nb, L, nd] (needed when z is given, else ignored); dh0 [nb, nd, N] (may be
+ * NULL).  Reductions over batch rows run in row order, so the result does not
+ * depend on nthreads. */
+ORACLE_API int oracle_selective_scan_bwd(const double* x, const double* delta, const double* A_log, const double* B,
+                                         const double* C, const double* D, const int32_t* valid_len,
+                                         const double* h0, int64_t nb, int64_t L, int64_t nd, int64_t N,
+                                         int softplus, int clamp, double dmin, double dmax,
+                                         const double* delta_bias, const double* z, const double* dy,
+                                         const double* dh_last, double* dx, double* ddelta, double* dA_log,
+                                         double* dB, double* dC, double* dD, double* ddelta_bias, double* dz,
+                                         double* dh0, int nthreads) {
+  if (nb < 0 || L < 0 || nd < 0 || N < 1 || !A_log || !dA_log) return -3;
+  if (L > 0 && (!x || !delta || !B || !C || !dy || !dx || !ddelta || !dB || !dC)) return -3;
+  if (z && !dz) return -3;
+  problem_t p = {x, delta, A_log, B, C, D, h0, valid_len, nb, L, nd, N, softplus, clamp, dmin, dmax,
+                 delta_bias, z, NULL, 1};
+  double* part = (double*)calloc((size_t)(nb * nd * N + 2 * nb * nd + 1), sizeof(double));
+  if (!part) return -1;
+  if (L > 0) {
+    memset(dB, 0, sizeof(double) * (size_t)(nb * L * N));
+    memset(dC, 0, sizeof(double) * (size_t)(nb * L * N));
+  }
+  bwd_job_t job = {&p, dy, dh_last, dx, ddelta, dB, dC, z ? dz : NULL, dh0,
+                   part, part + nb * nd * N, part + nb * nd * N + nb * nd, 1, 0};
+  if (nthreads < 1) nthreads = 1;
+  if (nthreads > 256) nthreads = 256;
+  if (nthreads > nb) nthreads = nb > 0 ? (int)nb : 1;
+  job.nthreads = nthreads;
+  pthread_t tid[256];
+  bwd_arg_t args[256];
+  int started = 0;
+  for (int k = 0; k < nthreads; ++k) {
+    args[k].job = &job;
+    args[k].k = k;
+    if (k == 0) continue;
+    if (pthread_create(&tid[k], NULL, bwd_worker, &args[k]) != 0) {
+      job.status = -2;
+      break;
+    }
+    started = k;
+  }
+  bwd_worker(&args[0]);
+  for (int k = 1; k <= started; ++k) pthread_join(tid[k], NULL);
+  if (job.status == -2) {
+    job.status = 0;
+    for (int k = started + 1; k < nthreads; ++k) bwd_worker(&args[k]);
+  }
+  if (job.status == 0) {
+    for (int64_t i = 0; i < nd * N; ++i) {
+      double s = 0.0;
+      for (int64_t b = 0; b < nb; ++b) s += job.dA_part[b * nd * N + i];
+      dA_log[i] = s;
+    }
+    for (int64_t d = 0; d < nd; ++d) {
+      double s = 0.0, sb = 0.0;
+      for (int64_t b = 0; b < nb; ++b) {
+        s += job.dD_part[b * nd + d];
+        sb += job.dbias_part[b * nd + d];
+      }
+      if (dD) dD[d] = s;
+      if (ddelta_bias) ddelta_bias[d] = sb;
+    }
+  }
+  free(part);
+  return job.status;
+}
+
 ORACLE_API int oracle_mutation_id(void) { return ORACLE_MUTATION; }

@@ -355,6 +355,117 @@ def pin_chunk_states(orc, mutation=0):
     assert np.array_equal(cs[:, -1], h)
 
 
+# ---- backward -------------------------------------------------------------
+
+def _loss(orc, mutation, x, delta, A_log, B, C, D, vl, h0, bias, z, dy, dhl, clamp=None):
+    y, h = orc.selective_scan(x, delta, A_log, B, C, D, valid_len=vl, h0=h0, delta_bias=bias, z=z,
+                              delta_clamp=clamp, mutation=mutation)
+    return float(np.sum(dy * y) + np.sum(dhl * h))
+
+
+def _bwd_problem(seed, clamp=False):
+    rng = np.random.default_rng(seed)
+    nb, L, nd, N = 2, 7, 3, 4
+    x, delta, A_log, B, C, D = _rand_problem(rng, nb, L, nd, N, bias=-1.0)
+    vl = np.array([L, 4], dtype=np.int32)
+    h0 = rng.standard_normal((nb, nd, N))
+    bias = 0.3 * rng.standard_normal(nd)
+    z = 1.5 * rng.standard_normal((nb, L, nd))
+    dy = rng.standard_normal((nb, L, nd))
+    dhl = rng.standard_normal((nb, nd, N))
+    if clamp:
+        # softplus values well inside or well outside [0.25, 0.6]: no kink within the difference step
+        sp = np.log1p(np.exp(delta + bias[None, None, :]))
+        near = (np.abs(sp - 0.25) < 0.02) | (np.abs(sp - 0.6) < 0.02)
+        delta = np.where(near, delta + 0.1, delta)
+    return x, delta, A_log, B, C, D, vl, h0, bias, z, dy, dhl
+
+
+def pin_bwd_finite_differences(orc, mutation=0):
+    """Every gradient of the backward against central differences of the
+    forward's loss sum(dy*y) + sum(dh_last*h_last), element by element, with
+    padding, initial state, delta bias, gate, and (second case) the clip."""
+    for seed, clamp in ((41, None), (43, (0.25, 0.6))):
+        x, delta, A_log, B, C, D, vl, h0, bias, z, dy, dhl = _bwd_problem(seed, clamp is not None)
+        g = orc.selective_scan_bwd(x, delta, A_log, B, C, D, dy, valid_len=vl, h0=h0, delta_bias=bias, z=z,
+                                   dh_last=dhl, delta_clamp=clamp, mutation=mutation)
+        args = dict(x=x, delta=delta, A_log=A_log, B=B, C=C, D=D, h0=h0, bias=bias, z=z)
+        names = dict(x="dx", delta="ddelta", A_log="dA_log", B="dB", C="dC", D="dD", h0="dh0", bias="ddelta_bias",
+                     z="dz")
+        eps = 1e-6
+        for k, arr in args.items():
+            fd = np.empty_like(arr)
+            for idx in np.ndindex(arr.shape):
+                plus, minus = arr.copy(), arr.copy()
+                plus[idx] += eps
+                minus[idx] -= eps
+                ap, am = dict(args, **{k: plus}), dict(args, **{k: minus})
+                lp = _loss(orc, mutation, ap["x"], ap["delta"], ap["A_log"], ap["B"], ap["C"], ap["D"], vl, ap["h0"],
+                           ap["bias"], ap["z"], dy, dhl, clamp)
+                lm = _loss(orc, mutation, am["x"], am["delta"], am["A_log"], am["B"], am["C"], am["D"], vl, am["h0"],
+                           am["bias"], am["z"], dy, dhl, clamp)
+                fd[idx] = (lp - lm) / (2 * eps)
+            got = g[names[k]]
+            scale = max(1.0, float(np.max(np.abs(fd))))
+            assert np.max(np.abs(got - fd)) <= 1e-6 * scale, (k, clamp, np.max(np.abs(got - fd)))
+
+
+def pin_bwd_linearity(orc, mutation=0):
+    """Exact identities of the linear parts (Euler's theorem for linear maps):
+    with delta, A, B, C, D fixed, y and h_last are linear in (x, h0) jointly, so
+    <dy, y> + <dh_last, h_last> = <dx, x> + <dh0, h0>; y - D x is linear in C,
+    so <dy, y - D x> = <dC, C>; from a zero state it is linear in B too, so
+    <dy, y - D x> = <dB, B>; and <dy, D x> = <dD, D>."""
+    rng = np.random.default_rng(47)
+    nb, L, nd, N = 2, 9, 3, 4
+    x, delta, A_log, B, C, D = _rand_problem(rng, nb, L, nd, N, bias=-1.0)
+    h0 = rng.standard_normal((nb, nd, N))
+    dy = rng.standard_normal((nb, L, nd))
+    dhl = rng.standard_normal((nb, nd, N))
+    y, h = orc.selective_scan(x, delta, A_log, B, C, D, h0=h0, mutation=mutation)
+    g = orc.selective_scan_bwd(x, delta, A_log, B, C, D, dy, h0=h0, dh_last=dhl, mutation=mutation)
+    lhs = np.sum(dy * y) + np.sum(dhl * h)
+    assert abs(lhs - (np.sum(g["dx"] * x) + np.sum(g["dh0"] * h0))) <= 1e-12 * max(1.0, abs(lhs))
+    ydx = y - D[None, None, :] * x
+    assert abs(np.sum(dy * ydx) - np.sum(g["dC"] * C)) <= 1e-12 * max(1.0, abs(np.sum(dy * ydx)))
+    assert abs(np.sum(dy * D[None, None, :] * x) - np.sum(g["dD"] * D)) <= 1e-12 * max(1.0, float(np.sum(np.abs(D))))
+    y0, _ = orc.selective_scan(x, delta, A_log, B, C, D, mutation=mutation)
+    g0 = orc.selective_scan_bwd(x, delta, A_log, B, C, D, dy, mutation=mutation)
+    y0dx = y0 - D[None, None, :] * x
+    assert abs(np.sum(dy * y0dx) - np.sum(g0["dB"] * B)) <= 1e-12 * max(1.0, abs(np.sum(dy * y0dx)))
+
+
+def pin_bwd_padding(orc, mutation=0):
+    """pwwt.cn section 2.3 in reverse: padded steps get zero gradients, garbage
+    in the padding changes nothing, and a padded row's gradients equal those of
+    the row run alone with its own length."""
+    rng = np.random.default_rng(53)
+    nb, L, nd, N = 3, 8, 2, 4
+    x, delta, A_log, B, C, D = _rand_problem(rng, nb, L, nd, N, bias=-1.0)
+    vl = np.array([8, 5, 0], dtype=np.int32)
+    dy = rng.standard_normal((nb, L, nd))
+    dhl = rng.standard_normal((nb, nd, N))
+    g = orc.selective_scan_bwd(x, delta, A_log, B, C, D, dy, valid_len=vl, dh_last=dhl, mutation=mutation)
+    for k in ("dx", "ddelta"):
+        assert np.all(g[k][1, 5:] == 0.0) and np.all(g[k][2] == 0.0)
+    assert np.all(g["dB"][1, 5:] == 0.0) and np.all(g["dC"][2] == 0.0)
+    assert np.array_equal(g["dh0"][2], dhl[2])  # nothing happens to an empty row's state
+    xg, dg, Bg, Cg = x.copy(), delta.copy(), B.copy(), C.copy()
+    xg[1, 5:] = np.nan
+    dg[1, 5:] = np.inf
+    Bg[2] = np.nan
+    Cg[1, 5:] = -np.inf
+    g2 = orc.selective_scan_bwd(xg, dg, A_log, Bg, Cg, D, dy, valid_len=vl, dh_last=dhl, mutation=mutation)
+    for k in g:
+        if g[k] is not None:
+            assert np.array_equal(g[k], g2[k]), k
+    g1 = orc.selective_scan_bwd(x[1:2, :5], delta[1:2, :5], A_log, B[1:2, :5], C[1:2, :5], D, dy[1:2, :5],
+                                dh_last=dhl[1:2], mutation=mutation)
+    for k in ("dx", "ddelta", "dB", "dC"):
+        assert np.array_equal(g1[k][0], g[k][1, :5]), k
+    assert np.array_equal(g1["dh0"][0], g["dh0"][1])
+
+
 ALL_PINS = {
     "closed_form_scan": pin_closed_form_scan,
     "closed_form_full_path": pin_closed_form_full_path,
@@ -370,6 +481,9 @@ ALL_PINS = {
     "delta_bias": pin_delta_bias,
     "output_gate": pin_output_gate,
     "chunk_states": pin_chunk_states,
+    "bwd_finite_differences": pin_bwd_finite_differences,
+    "bwd_linearity": pin_bwd_linearity,
+    "bwd_padding": pin_bwd_padding,
 }
 
 # The planted mistakes (see ssm_oracle.c) and the pins expected to notice each.
@@ -384,4 +498,7 @@ MUTATIONS = {
     8: ("B and C swapped in the input term", {"bruteforce_full"}),
     9: ("output gate applied before the skip term", {"output_gate"}),
     10: ("delta bias added after softplus", {"delta_bias"}),
+    11: ("backward: adjoint not decayed through the step", {"bwd_finite_differences", "bwd_linearity"}),
+    12: ("backward: dA without the delta factor", {"bwd_finite_differences"}),
+    13: ("backward: softplus derivative missing", {"bwd_finite_differences"}),
 }
