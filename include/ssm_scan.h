@@ -113,7 +113,9 @@ int ssm_selective_scan_fwd(ssm_scan_t handle, const void* x, const void* delta, 
  *               chunk may be shorter; past valid_len the state no longer
  *               changes) -- the boundary states kept for recomputation in the
  *               pwwt.cn article, section 3.4.
- *  chunk_len    must equal ssm_scan_chunk_len(dstate) when chunk_states is set.
+ *  chunk_len    when chunk_states is set: a multiple of 4 that divides
+ *               ssm_scan_chunk_len(dstate) (that value itself, the kernel's
+ *               time tile, is the coarsest choice), else SSM_ERR_INVALID_ARG.
  *
  *  time_parts, workspace, workspace_bytes: cut the time axis into parts that
  *               run on different workgroups (the multi-block chunked scan of
@@ -146,8 +148,9 @@ typedef struct ssm_scan_fwd_extras {
   int64_t workspace_bytes;
 } ssm_scan_fwd_extras;
 
-/* Steps per chunk of chunk_states for this dstate (the kernel's time tile):
- * 128, 64 or 32 for dstate 16, 32 or 64; 0 for an unsupported dstate. */
+/* The kernel's time tile for this dstate -- the coarsest chunk_len of
+ * chunk_states: 128, 64 or 32 for dstate 16, 32 or 64; 0 for an unsupported
+ * dstate. */
 int64_t ssm_scan_chunk_len(int64_t dstate);
 
 /* The number of time parts the library picks for these dims on the handle's

@@ -149,6 +149,9 @@ def chunk_len(dstate: int) -> int:
     return int(lib().ssm_scan_chunk_len(int(dstate)))
 
 
+_default_chunk_len = chunk_len  # the parameter of selective_scan_fwd shadows the name
+
+
 def auto_time_parts(handle, dims: ssm_scan_dims) -> int:
     """The time split the library picks for these dims on the handle's GPU."""
     return int(lib().ssm_scan_auto_time_parts(handle, ctypes.byref(dims)))
@@ -176,7 +179,8 @@ def handle_for(device_index: int) -> int:
 
 def selective_scan_fwd(x, delta, A_log, B, C, D=None, valid_len=None, *, delta_softplus: bool = True,
                        delta_clamp=None, y=None, h_last=None, return_h_last: bool = True, h0=None, delta_bias=None,
-                       z=None, return_chunk_states: bool = False, time_parts=None, workspace=None, stream=None):
+                       z=None, return_chunk_states: bool = False, chunk_len=None, time_parts=None, workspace=None,
+                       stream=None):
     """Selective-scan forward on the GPU.  Returns ``(y, h_last)``, or
     ``(y, h_last, chunk_states)`` with ``return_chunk_states``.
 
@@ -191,7 +195,8 @@ def selective_scan_fwd(x, delta, A_log, B, C, D=None, valid_len=None, *, delta_s
     Extras: h0 [batch, dim, dstate] float32 initial state (may be h_last
     itself); delta_bias [dim] float32 added to delta before softplus; z like x,
     output gate y * silu(z); chunk states [batch, ceil(L / chunk_len(dstate)),
-    dim, dstate] float32, the state after every chunk.
+    dim, dstate] float32, the state after every chunk (``chunk_len`` steps, a
+    multiple of 4 dividing chunk_len(dstate); default chunk_len(dstate)).
 
     Time split: ``time_parts`` None lets the library choose (it splits only
     batches too small to fill the GPU), 1 never splits, P >= 2 asks for at most
@@ -243,7 +248,7 @@ def selective_scan_fwd(x, delta, A_log, B, C, D=None, valid_len=None, *, delta_s
     if z is not None and (tuple(z.shape) != (nb, L, nd) or z.dtype != x.dtype or z.device != dev
                           or not z.is_contiguous()):
         raise ValueError("z must be a contiguous tensor like x")
-    cl = chunk_len(N)
+    cl = _default_chunk_len(N) if chunk_len is None else int(chunk_len)
     chunk_states = None
     if return_chunk_states:
         chunk_states = torch.empty((nb, (L + cl - 1) // cl, nd, N), dtype=torch.float32, device=dev)

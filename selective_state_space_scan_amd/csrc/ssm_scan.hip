@@ -65,6 +65,7 @@ struct FwdParams {
   const float* delta_bias;
   const void* z;
   float* chunk_states;
+  int64_t chunk_len;  // steps per chunk of chunk_states: a multiple of K dividing the tile
   // Time split across workgroups: the sequence is cut into n_parts parts of
   // part_len steps (a multiple of the tile; part_len = L when unsplit).  ws
   // holds, per part boundary, what the fold kernel leaves for the next parts.
@@ -361,16 +362,18 @@ __global__ __launch_bounds__(64 * W, kMinWavesPerSimd) void ssm_fwd_kernel(FwdPa
   float part_sd[PPL];  // FOLD, part >= 1: the part's delta sum for the pair's channel
 #pragma unroll
   for (int k = 0; k < PPL; ++k) part_sd[k] = 0.0f;
-  // Chunk-boundary states: the carry after each tile (tiles are numbered from
-  // the start of the sequence; a part starts on a tile boundary).
-  const int64_t n_chunks = (p.L + T - 1) / T;
-  const int64_t tile0 = t_begin / T;
-  auto store_chunk_state = [&](int64_t tile) {
-    if (FOLD || p.chunk_states == nullptr) return;
-    float* cb = p.chunk_states + ((static_cast<int64_t>(b) * n_chunks + tile0 + tile) * nd + cg * 16) * N;
-#pragma unroll
-    for (int k = 0; k < PPL; ++k)
-      if (pair_valid(k)) cb[pair_offset(k)] = carry[k];
+  // Chunk-boundary states: the state after the last step of every chunk of
+  // chunk_len steps (chunks are numbered from the start of the sequence; a
+  // chunk boundary is always a sub-chunk boundary, and a part starts on a tile
+  // boundary).  The last chunk may end past L: past the valid length the state
+  // no longer changes.
+  const int64_t n_chunks = (p.L + p.chunk_len - 1) / p.chunk_len;
+  const bool want_chunks = !FOLD && p.chunk_states != nullptr;
+  const int clj = static_cast<int>(p.chunk_len / K);  // sub-chunks per chunk (divides SUB)
+  // Stores pair k's state as that of chunk ci (ignored past the last chunk).
+  auto store_chunk = [&](int64_t ci, int k, float v) {
+    if (ci < n_chunks)
+      p.chunk_states[((static_cast<int64_t>(b) * n_chunks + ci) * nd + cg * 16) * N + pair_offset(k)] = v;
   };
 
   // Buffer resources of this batch row's x, delta, y, B and C, and the lane's
@@ -513,7 +516,21 @@ __global__ __launch_bounds__(64 * W, kMinWavesPerSimd) void ssm_fwd_kernel(FwdPa
       }
     }
     if constexpr (FOLD) return;  // the next tile's pass 1 writes the other record buffer
-    store_chunk_state(t_tile / T);
+    if (want_chunks) {
+      // The state after sub-chunk jj is the one the walk left for sub-chunk
+      // jj + 1 (this lane's own LDS writes), or the carry after the last.
+      const int64_t ci0 = (t_begin + t_tile) / p.chunk_len;
+#pragma unroll
+      for (int k = 0; k < PPL; ++k) {
+        if (pair_valid(k)) {
+          int cc, n;
+          pair_of(k, cc, n);
+          const float* pbw = agg_b[buf] + ((n / 4) * 16 + cc) * 4 + (n % 4);
+          for (int jj = clj - 1; jj < SUB; jj += clj)
+            store_chunk(ci0 + (jj + 1) / clj - 1, k, jj == SUB - 1 ? carry[k] : pbw[(jj + 1) * (N / 4) * 64]);
+        }
+      }
+    }
     __syncthreads();
 
     // ---- pass 2: states from the incoming state, readout ----
@@ -591,7 +608,13 @@ __global__ __launch_bounds__(64 * W, kMinWavesPerSimd) void ssm_fwd_kernel(FwdPa
   } else {
     // Tiles wholly in the padding: the carry is unchanged and y is +0.
     for (; t_next < L; t_next += T) {
-      store_chunk_state(t_next / T);
+      if (want_chunks) {
+        const int64_t ci0 = (t_begin + t_next) / p.chunk_len;
+#pragma unroll
+        for (int k = 0; k < PPL; ++k)
+          if (pair_valid(k))
+            for (int jj = clj - 1; jj < SUB; jj += clj) store_chunk(ci0 + (jj + 1) / clj - 1, k, carry[k]);
+      }
       const int64_t left = L - t_next - j * K;
 #pragma unroll
       for (int i = 0; i < K; ++i) {
@@ -664,6 +687,11 @@ hipError_t launch(const FwdParams& prm, hipStream_t stream) {
 template <int G>
 constexpr int64_t tile_steps_g = Config<uint16_t, G>::W * (4 / G) * Config<uint16_t, G>::K;
 static_assert(tile_steps_g<1> == Config<float, 1>::W * 4 * Config<float, 1>::K, "tile must not depend on io");
+// The host accepts chunk lengths that are multiples of 4: every configuration
+// uses 4-step sub-chunks.
+static_assert(Config<uint16_t, 1>::K == 4 && Config<uint16_t, 2>::K == 4 && Config<uint16_t, 4>::K == 4 &&
+                  Config<float, 1>::K == 4 && Config<float, 2>::K == 4 && Config<float, 4>::K == 4,
+              "chunk boundaries are sub-chunk boundaries");
 
 int64_t tile_steps(int64_t N) {
   switch (N) {
@@ -846,7 +874,10 @@ int ssm_selective_scan_fwd_ex(ssm_scan_t handle, const void* x, const void* delt
 
   const ssm_scan_fwd_extras none = {nullptr, nullptr, nullptr, nullptr, 0, 0, nullptr, 0};
   const ssm_scan_fwd_extras& ex = extras ? *extras : none;
-  if (ex.chunk_states != nullptr && ex.chunk_len != tile_steps(N)) return SSM_ERR_INVALID_ARG;
+  // chunk_len: a multiple of the 4-step sub-chunk that divides the tile
+  if (ex.chunk_states != nullptr &&
+      (ex.chunk_len < 4 || ex.chunk_len % 4 != 0 || tile_steps(N) % ex.chunk_len != 0))
+    return SSM_ERR_INVALID_ARG;
   if (ex.time_parts < 0 || ex.workspace_bytes < 0 || (ex.workspace == nullptr && ex.workspace_bytes != 0))
     return SSM_ERR_INVALID_ARG;
   // An explicit split needs its workspace; the automatic one is skipped when
@@ -860,7 +891,8 @@ int ssm_selective_scan_fwd_ex(ssm_scan_t handle, const void* x, const void* delt
   const size_t e = static_cast<size_t>(esz);
   const size_t n_xd = static_cast<size_t>(nb) * L * nd, n_bc = static_cast<size_t>(nb) * L * N;
   const size_t n_state = static_cast<size_t>(nb) * nd * N;
-  const size_t n_chunks = L > 0 ? static_cast<size_t>((L + tile_steps(N) - 1) / tile_steps(N)) : 0;
+  const int64_t cl = ex.chunk_states != nullptr ? ex.chunk_len : tile_steps(N);
+  const size_t n_chunks = (L > 0 && cl > 0) ? static_cast<size_t>((L + cl - 1) / cl) : 0;
   if (!empty) {
     if (A_log == nullptr) return SSM_ERR_INVALID_ARG;
     if (L > 0 && (x == nullptr || delta == nullptr || B == nullptr || C == nullptr || y == nullptr))
@@ -934,6 +966,7 @@ int ssm_selective_scan_fwd_ex(ssm_scan_t handle, const void* x, const void* delt
   prm.delta_bias = ex.delta_bias;
   prm.z = ex.z;
   prm.chunk_states = ex.chunk_states;
+  prm.chunk_len = ex.chunk_states != nullptr ? ex.chunk_len : tile_steps(N);
   prm.L = L;
   prm.nb = static_cast<int32_t>(nb);
   prm.nd = static_cast<int32_t>(nd);

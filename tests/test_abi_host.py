@@ -115,8 +115,13 @@ def test_extras_checks():
     # NULL extras and all-NULL extras reach the handle check
     assert _ex_call(_dims(), None) == ssm.SSM_ERR_INVALID_ARG
     assert _ex_call(_dims(), E()) == ssm.SSM_ERR_INVALID_ARG
-    # chunk states need the kernel's chunk length
-    assert _ex_call(_dims(), E(chunk_states=8 * MB, chunk_len=64)) == ssm.SSM_ERR_INVALID_ARG
+    # chunk states: a multiple of 4 that divides the tile (128 at dstate 16)
+    for bad in (0, -4, 2, 6, 12, 256):
+        assert _ex_call(_dims(), E(chunk_states=8 * MB, chunk_len=bad)) == ssm.SSM_ERR_INVALID_ARG, bad
+    bad_x = dict(x=PTRS["x"] + 1)  # fails the later alignment check when the chunk length is accepted
+    for good in (4, 8, 16, 32, 64, 128):
+        assert _ex_call(_dims(), E(chunk_states=8 * MB, chunk_len=good), **bad_x) == ssm.SSM_ERR_UNSUPPORTED, good
+    assert _ex_call(_dims(dstate=64), E(chunk_states=8 * MB, chunk_len=64), **bad_x) == ssm.SSM_ERR_INVALID_ARG
     # misaligned extras
     assert _ex_call(_dims(), E(h0=8 * MB + 2)) == ssm.SSM_ERR_UNSUPPORTED
     assert _ex_call(_dims(io=ssm.SSM_IO_BF16), E(z=8 * MB + 1)) == ssm.SSM_ERR_UNSUPPORTED

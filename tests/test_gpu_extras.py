@@ -68,16 +68,16 @@ def test_extras_against_oracle(io, N, use):
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-@pytest.mark.parametrize("N", [16, 64])
-def test_chunk_states_against_oracle(io, N):
+@pytest.mark.parametrize("N,div", [(16, 1), (64, 1), (16, 2), (16, 32), (32, 4), (64, 2), (64, 8)])
+def test_chunk_states_against_oracle(io, N, div):
     import selective_state_space_scan_amd as ssm
-    w, inp = _case(io, N, L=1000, seed=7 * N, varlen=True)
-    cl = ssm.chunk_len(N)
-    y, h, cs = _gpu(inp, io, ("h0", "z"), chunks=True)
+    w, inp = _case(io, N, L=1000, seed=7 * N + div, varlen=True)
+    cl = ssm.chunk_len(N) // div
+    y, h, cs = _gpu(inp, io, ("h0", "z"), chunks=True, chunk_len=cl)
     yr, hr, csr = _oracle(inp, ("h0", "z"), chunk_len=cl)
     assert cs.shape == csr.shape
     ecs = rel_err(to_np64(cs), csr)
-    print(f"{io} N={N} chunk states err {ecs:.2e}", flush=True)
+    print(f"{io} N={N} chunk_len {cl}: chunk states err {ecs:.2e}", flush=True)
     assert ecs <= tol_for(io)
     assert np.array_equal(_bits(cs[:, -1]), _bits(h))  # the last chunk state is h_last
     # a row with no valid steps keeps h0 in every chunk state
