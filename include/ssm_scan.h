@@ -171,6 +171,70 @@ int ssm_selective_scan_fwd_ex(ssm_scan_t handle, const void* x, const void* delt
                               const void* C, const float* D, const int32_t* valid_len, void* y, float* h_last,
                               const ssm_scan_dims* dims, const ssm_scan_fwd_extras* extras, void* stream);
 
+/* ---- backward --------------------------------------------------------
+ *
+ * Gradients of the forward for the loss sum(dy * y) + sum(dh_last * h_last),
+ * by reverse-mode differentiation of the recurrence: the adjoint of the state
+ * runs backwards in time (the same affine scan on flipped time, pwwt.cn
+ * sections 2.1 and 3.1), and the forward states are recomputed tile by tile
+ * from the chunk-boundary states the forward saved (its section 3.4).  x,
+ * delta, A_log, B, C, D, valid_len, dims and the extras (h0, delta_bias, z;
+ * the other extras fields are ignored) must be those of the forward.
+ *
+ *  dy            [batch, seqlen, dim] io dtype: gradient of y (the gated y
+ *                when z is given).
+ *  dh_last       [batch, dim, dstate] fp32 or NULL (zero).
+ *  chunk_states  the forward's chunk_states with chunk_len =
+ *                ssm_scan_bwd_chunk_len(dstate) (only the first
+ *                ceil(seqlen / chunk_len) - 1 are read; NULL allowed when
+ *                seqlen <= chunk_len).
+ *  dx, ddelta    [batch, seqlen, dim] io dtype: gradients of x and of the raw
+ *                delta (before bias, softplus and clip); +0 at padded steps.
+ *  dz            [batch, seqlen, dim] io dtype, required when z is given.
+ *  dA_log        [dim, dstate] fp32.
+ *  dB, dC        [batch, seqlen, dstate] fp32; zero at padded steps.
+ *  dD, ddelta_bias [dim] fp32 or NULL.
+ *  dh0           [batch, dim, dstate] fp32 or NULL: gradient of the initial
+ *                state.
+ *  workspace     at least ssm_scan_bwd_workspace_bytes(dims) bytes of device
+ *                scratch (4-byte aligned), overwritten; it holds per channel
+ *                group partial sums of dB and dC that a second kernel adds in
+ *                a fixed order, so the result is deterministic.
+ * No output may overlap an input or another output. */
+typedef struct ssm_scan_bwd_io {
+  const void* dy;
+  const float* dh_last;
+  const float* chunk_states;
+  void* dx;
+  void* ddelta;
+  void* dz;
+  float* dA_log;
+  float* dB;
+  float* dC;
+  float* dD;
+  float* ddelta_bias;
+  float* dh0;
+  void* workspace;
+  int64_t workspace_bytes;
+} ssm_scan_bwd_io;
+
+/* The backward's time tile for this dstate (64, 32 or 16 for dstate 16, 32 or
+ * 64; 0 if unsupported): the chunk_len the forward must save chunk_states at. */
+int64_t ssm_scan_bwd_chunk_len(int64_t dstate);
+
+/* Workspace bytes of ssm_selective_scan_bwd for these dims: 4 * (2 * (dim/16)
+ * * batch * seqlen * dstate + batch * dim * dstate + 2 * batch * dim); -1 for
+ * NULL or invalid dims. */
+int64_t ssm_scan_bwd_workspace_bytes(const ssm_scan_dims* dims);
+
+/* Enqueue the backward on `stream` (two kernels).  Same conventions as the
+ * forward: host-side checks first (SSM_ERR_INVALID_ARG also for a missing
+ * required output, chunk_states or workspace, or a workspace that is too
+ * small), nothing enqueued on failure, bitwise reproducible results. */
+int ssm_selective_scan_bwd(ssm_scan_t handle, const void* x, const void* delta, const float* A_log, const void* B,
+                           const void* C, const float* D, const int32_t* valid_len, const ssm_scan_dims* dims,
+                           const ssm_scan_fwd_extras* extras, const ssm_scan_bwd_io* io, void* stream);
+
 /* Release the handle.  NULL is accepted.  The caller must ensure no work
  * enqueued with the handle is still to be launched. */
 int ssm_scan_destroy(ssm_scan_t handle);

@@ -26,7 +26,8 @@ SSM_IO_BF16 = 1
 
 # Names declared in include/ssm_scan.h.
 EXPORTED = ("ssm_scan_create", "ssm_selective_scan_fwd", "ssm_selective_scan_fwd_ex", "ssm_scan_chunk_len",
-            "ssm_scan_auto_time_parts", "ssm_scan_workspace_bytes", "ssm_scan_destroy", "ssm_scan_error_string")
+            "ssm_scan_auto_time_parts", "ssm_scan_workspace_bytes", "ssm_scan_bwd_chunk_len",
+            "ssm_scan_bwd_workspace_bytes", "ssm_selective_scan_bwd", "ssm_scan_destroy", "ssm_scan_error_string")
 
 
 class SsmScanError(RuntimeError):
@@ -57,6 +58,25 @@ class ssm_scan_fwd_extras(ctypes.Structure):
         ("chunk_states", ctypes.c_void_p),
         ("chunk_len", ctypes.c_int64),
         ("time_parts", ctypes.c_int32),
+        ("workspace", ctypes.c_void_p),
+        ("workspace_bytes", ctypes.c_int64),
+    ]
+
+
+class ssm_scan_bwd_io(ctypes.Structure):
+    _fields_ = [
+        ("dy", ctypes.c_void_p),
+        ("dh_last", ctypes.c_void_p),
+        ("chunk_states", ctypes.c_void_p),
+        ("dx", ctypes.c_void_p),
+        ("ddelta", ctypes.c_void_p),
+        ("dz", ctypes.c_void_p),
+        ("dA_log", ctypes.c_void_p),
+        ("dB", ctypes.c_void_p),
+        ("dC", ctypes.c_void_p),
+        ("dD", ctypes.c_void_p),
+        ("ddelta_bias", ctypes.c_void_p),
+        ("dh0", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_int64),
     ]
@@ -105,6 +125,13 @@ def lib() -> ctypes.CDLL:
         L.ssm_scan_auto_time_parts.restype = ctypes.c_int32
         L.ssm_scan_workspace_bytes.argtypes = [ctypes.POINTER(ssm_scan_dims), ctypes.c_int32]
         L.ssm_scan_workspace_bytes.restype = ctypes.c_int64
+        L.ssm_scan_bwd_chunk_len.argtypes = [ctypes.c_int64]
+        L.ssm_scan_bwd_chunk_len.restype = ctypes.c_int64
+        L.ssm_scan_bwd_workspace_bytes.argtypes = [ctypes.POINTER(ssm_scan_dims)]
+        L.ssm_scan_bwd_workspace_bytes.restype = ctypes.c_int64
+        L.ssm_selective_scan_bwd.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, ctypes.POINTER(ssm_scan_dims),
+                                             ctypes.POINTER(ssm_scan_fwd_extras), ctypes.POINTER(ssm_scan_bwd_io), vp]
+        L.ssm_selective_scan_bwd.restype = ctypes.c_int
         _lib = L
         return L
 
@@ -150,6 +177,22 @@ def chunk_len(dstate: int) -> int:
 
 
 _default_chunk_len = chunk_len  # the parameter of selective_scan_fwd shadows the name
+
+
+def bwd_chunk_len(dstate: int) -> int:
+    """The chunk length the forward must save chunk states at for the backward."""
+    return int(lib().ssm_scan_bwd_chunk_len(int(dstate)))
+
+
+def bwd_workspace_bytes(dims: ssm_scan_dims) -> int:
+    return int(lib().ssm_scan_bwd_workspace_bytes(ctypes.byref(dims)))
+
+
+def ssm_selective_scan_bwd(handle, x, delta, A_log, B, C, D, valid_len, dims: ssm_scan_dims,
+                           extras: ssm_scan_fwd_extras | None, io: ssm_scan_bwd_io, stream) -> int:
+    """The backward entry point (raw pointers); returns the status code."""
+    return lib().ssm_selective_scan_bwd(handle, x, delta, A_log, B, C, D, valid_len, ctypes.byref(dims),
+                                        None if extras is None else ctypes.byref(extras), ctypes.byref(io), stream)
 
 
 def auto_time_parts(handle, dims: ssm_scan_dims) -> int:
@@ -297,3 +340,87 @@ def selective_scan_fwd(x, delta, A_log, B, C, D=None, valid_len=None, *, delta_s
     if return_chunk_states:
         return y, h_last, chunk_states
     return y, h_last
+
+
+def selective_scan_bwd(x, delta, A_log, B, C, D, valid_len, dy, chunk_states, *, dh_last=None, h0=None,
+                       delta_bias=None, z=None, delta_softplus: bool = True, delta_clamp=None, workspace=None,
+                       stream=None) -> dict:
+    """Gradients of ``selective_scan_fwd`` for the loss sum(dy * y) + sum(dh_last * h_last).
+
+    The forward inputs and flags must be the ones of the forward call, and
+    ``chunk_states`` that call's chunk states saved with
+    ``chunk_len=bwd_chunk_len(dstate)`` (None is accepted when L fits one
+    chunk).  Returns a dict: dx, ddelta (w.r.t. the raw delta) and dz (None
+    without z) like x; dA_log [dim, dstate], dB, dC [batch, L, dstate], dD and
+    ddelta_bias [dim] (None when D / delta_bias is None) and dh0 [batch, dim,
+    dstate], all float32.  Asynchronous on ``stream``.
+    """
+    import torch
+
+    if x.device.type != "cuda":
+        raise ValueError("tensors must be on a GPU device")
+    dev = x.device
+    io = {torch.float32: SSM_IO_F32, torch.bfloat16: SSM_IO_BF16}.get(x.dtype)
+    if io is None or x.dim() != 3:
+        raise ValueError("x must be a [batch, L, dim] float32 or bfloat16 tensor")
+    nb, L, nd = x.shape
+    N = A_log.shape[1]
+    for name, t, shape, dt in (("delta", delta, (nb, L, nd), x.dtype), ("B", B, (nb, L, N), x.dtype),
+                               ("C", C, (nb, L, N), x.dtype), ("A_log", A_log, (nd, N), torch.float32),
+                               ("dy", dy, (nb, L, nd), x.dtype)):
+        if tuple(t.shape) != shape or t.dtype != dt or t.device != dev or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous {shape} {dt} tensor on {dev}")
+    cl = bwd_chunk_len(N)
+    n_chunks = (L + cl - 1) // cl if cl > 0 else 0
+    if chunk_states is not None and (tuple(chunk_states.shape) != (nb, n_chunks, nd, N)
+                                     or chunk_states.dtype != torch.float32 or not chunk_states.is_contiguous()):
+        raise ValueError(f"chunk_states must be [batch, {n_chunks}, dim, dstate] float32 "
+                         f"(the forward's, with chunk_len={cl})")
+    for name, t, shape in (("dh_last", dh_last, (nb, nd, N)), ("h0", h0, (nb, nd, N)),
+                           ("delta_bias", delta_bias, (nd,)), ("D", D, (nd,))):
+        if t is not None and (tuple(t.shape) != shape or t.dtype != torch.float32 or t.device != dev
+                              or not t.is_contiguous()):
+            raise ValueError(f"{name} must be a contiguous {shape} float32 tensor on {dev}")
+    if z is not None and (tuple(z.shape) != (nb, L, nd) or z.dtype != x.dtype or not z.is_contiguous()):
+        raise ValueError("z must be a contiguous tensor like x")
+    out = dict(dx=torch.empty_like(x), ddelta=torch.empty_like(x), dz=torch.empty_like(x) if z is not None else None,
+               dA_log=torch.empty((nd, N), dtype=torch.float32, device=dev),
+               dB=torch.empty((nb, L, N), dtype=torch.float32, device=dev),
+               dC=torch.empty((nb, L, N), dtype=torch.float32, device=dev),
+               dD=torch.empty(nd, dtype=torch.float32, device=dev) if D is not None else None,
+               ddelta_bias=torch.empty(nd, dtype=torch.float32, device=dev) if delta_bias is not None else None,
+               dh0=torch.empty((nb, nd, N), dtype=torch.float32, device=dev))
+    dims = ssm_scan_dims()
+    dims.batch, dims.seqlen, dims.dim, dims.dstate = nb, L, nd, N
+    dims.io_dtype = io
+    dims.delta_softplus = 1 if delta_softplus else 0
+    if delta_clamp is not None:
+        dims.delta_clamp = 1
+        dims.delta_min, dims.delta_max = float(delta_clamp[0]), float(delta_clamp[1])
+    if stream is None:
+        stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+    def ptr(t):
+        return None if t is None or t.numel() == 0 else t.data_ptr()
+
+    nbytes = bwd_workspace_bytes(dims)
+    if nbytes < 0:
+        raise ValueError("unsupported dims for the backward")
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 4), dtype=torch.uint8, device=dev)
+        if hasattr(stream, "cuda_stream"):
+            workspace.record_stream(stream)
+    elif workspace.dtype != torch.uint8 or workspace.numel() < nbytes or not workspace.is_contiguous():
+        raise ValueError(f"workspace must be a contiguous uint8 tensor of at least {nbytes} bytes")
+    extras = ssm_scan_fwd_extras(ptr(h0), ptr(delta_bias), ptr(z), None, 0, 0, None, 0)
+    bio = ssm_scan_bwd_io(ptr(dy), ptr(dh_last), ptr(chunk_states), ptr(out["dx"]), ptr(out["ddelta"]),
+                          ptr(out["dz"]), ptr(out["dA_log"]), ptr(out["dB"]), ptr(out["dC"]), ptr(out["dD"]),
+                          ptr(out["ddelta_bias"]), ptr(out["dh0"]), ptr(workspace), max(nbytes, 4))
+    with torch.cuda.device(dev):
+        h = handle_for(dev.index if dev.index is not None else torch.cuda.current_device())
+        rc = ssm_selective_scan_bwd(h, ptr(x), ptr(delta), ptr(A_log), ptr(B), ptr(C), ptr(D), ptr(valid_len),
+                                    dims, extras, bio, sptr)
+    if rc != SSM_OK:
+        raise SsmScanError(rc, "ssm_selective_scan_bwd")
+    return out

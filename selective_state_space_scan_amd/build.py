@@ -1,6 +1,7 @@
 """Compiles the HIP library (``libssmscan.so``) for gfx950 in-tree.
 
-The build is a single hipcc invocation; it always recompiles when called.
+The build is a single hipcc invocation over the forward and backward sources;
+it always recompiles when called.
 Packed fp32 VALU instructions are disabled for every HIP source
 (``-target-feature -packed-fp32-ops``).
 """
@@ -13,7 +14,7 @@ import sys
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 REPO_DIR = os.path.dirname(PKG_DIR)
-SRC = os.path.join(PKG_DIR, "csrc", "ssm_scan.hip")
+SRCS = [os.path.join(PKG_DIR, "csrc", f) for f in ("ssm_scan.hip", "ssm_scan_bwd.hip")]
 INCLUDE_DIR = os.path.join(REPO_DIR, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libssmscan.so")
 ARCH = "gfx950"
@@ -31,7 +32,7 @@ def compile_command(out: str = LIB_PATH) -> list[str]:
         hipcc(), "-O3", "-std=c++20", f"--offload-arch={ARCH}",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-fPIC", "-shared", "-Wall", f"-I{INCLUDE_DIR}",
-        "-o", out, SRC,
+        "-o", out, *[s for s in SRCS if os.path.exists(s)],
     ]
 
 

@@ -1,0 +1,171 @@
+// Internals shared by the forward and backward sources of the HIP library:
+// the handle, buffer-resource element access, and the device math helpers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+struct ssm_scan_handle_s {
+  int device;
+  int cu_count;
+};
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// ---- element access ------------------------------------------------------
+//
+// Every tensor row a workgroup touches is addressed through a buffer resource
+// (base in SGPRs) with a fixed per-lane byte offset in a VGPR and the per-step
+// offset in an SGPR, so the hot loop does no per-lane address arithmetic.  The
+// host guarantees that a row spans fewer than 2^31 bytes.
+
+using rsrc_t = __amdgpu_buffer_rsrc_t;
+
+// Word 3 of a gfx9 buffer resource: 32-bit data format, everything else zero.
+constexpr int kRsrcWord3 = 0x00020000;
+// Cache policy bits of buffer instructions: non-temporal for data streamed once.
+constexpr int kStream = 2;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, static_cast<int>(bytes), kRsrcWord3);
+}
+
+template <typename IO>
+struct Elem;
+
+template <>
+struct Elem<float> {
+  static constexpr int kBytes = 4;
+  template <int AUX>
+  static __device__ __forceinline__ float load(rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, AUX));
+  }
+  static __device__ __forceinline__ void store(rsrc_t r, uint32_t voff, uint32_t soff, float v) {
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, voff, soff, kStream);
+  }
+};
+
+// bf16 is carried as its 16-bit pattern; widening to fp32 is exact.
+template <>
+struct Elem<uint16_t> {
+  static constexpr int kBytes = 2;
+  template <int AUX>
+  static __device__ __forceinline__ float load(rsrc_t r, uint32_t voff, uint32_t soff) {
+    const uint32_t u = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, AUX);
+    return __builtin_bit_cast(float, u << 16);
+  }
+  static __device__ __forceinline__ void store(rsrc_t r, uint32_t voff, uint32_t soff, float v) {
+    // v_cvt_pk_bf16_f32: round to nearest even.
+    const __bf16 h = static_cast<__bf16>(v);
+    __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, h), r, voff, soff, kStream);
+  }
+};
+
+// ---- math ----------------------------------------------------------------
+
+__device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
+
+// softplus(v) = max(v, 0) + log1p(exp(-|v|)).  log1p(e) is evaluated as
+// log(w) * e / (w - 1) with w = 1 + e, the correction that makes log(1 + e)
+// accurate for small e (D. Goldberg, "What every computer scientist should know
+// about floating-point arithmetic", 1991, theorem 4); when w rounds to 1,
+// log1p(e) = e to working precision.
+__device__ __forceinline__ float softplus_f32(float v) {
+  const float e = fast_exp2(-__builtin_fabsf(v) * kLog2e);
+  const float w = 1.0f + e;
+  const float wm1 = w - 1.0f;
+  const float lg = __builtin_amdgcn_logf(w) * kLn2;  // v_log_f32 is log2
+  const float l1p = (wm1 == 0.0f) ? e : lg * (e * __builtin_amdgcn_rcpf(wm1));
+  return __builtin_fmaxf(v, 0.0f) + l1p;
+}
+
+// DPP row_newbcast:S -- every lane of a 16-lane row reads lane S of that row.
+template <int S>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x150 + S, 0xf, 0xf, true));
+}
+
+// y_m += C[s] * h[s] for s % 4 == m over the 16 states (four accumulators, so
+// that consecutive instructions do not depend on each other), C[s] taken from
+// lane s of the row by DPP row_newbcast fused into v_fmac_f32 (the compiler
+// does not fuse a DPP move into v_fmac, so this is written out).  The leading
+// s_nop covers the DPP hazards (a VALU write of the DPP source needs 2 wait
+// states before the read, a VALU write of EXEC needs 5); c is not written
+// inside the block.
+__device__ __forceinline__ void dot16_row_bcast(float (&y)[4], float c, const float (&h)[16]) {
+  asm volatile(
+      "s_nop 4\n\t"
+      "v_fmac_f32_dpp %0, %4, %5 row_newbcast:0 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %4, %6 row_newbcast:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %4, %7 row_newbcast:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %4, %8 row_newbcast:3 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %4, %9 row_newbcast:4 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %4, %10 row_newbcast:5 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %4, %11 row_newbcast:6 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %4, %12 row_newbcast:7 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %4, %13 row_newbcast:8 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %4, %14 row_newbcast:9 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %4, %15 row_newbcast:10 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %4, %16 row_newbcast:11 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %0, %4, %17 row_newbcast:12 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %1, %4, %18 row_newbcast:13 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %2, %4, %19 row_newbcast:14 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %4, %20 row_newbcast:15 row_mask:0xf bank_mask:0xf"
+      : "+v"(y[0]), "+v"(y[1]), "+v"(y[2]), "+v"(y[3])
+      : "v"(c), "v"(h[0]), "v"(h[1]), "v"(h[2]), "v"(h[3]), "v"(h[4]), "v"(h[5]), "v"(h[6]), "v"(h[7]),
+        "v"(h[8]), "v"(h[9]), "v"(h[10]), "v"(h[11]), "v"(h[12]), "v"(h[13]), "v"(h[14]), "v"(h[15]));
+}
+
+// Sum of v over the G state-group rows that share a time sub-chunk; every lane
+// of those rows gets the same bits (fixed order: (r0 + r1) + (r2 + r3)).
+// v_permlane16_swap exchanges rows 0<->1 and 2<->3 between its two operands,
+// v_permlane32_swap the two 32-lane halves; starting both operands from the
+// same value leaves each lane with its own value and its partner's.  Written
+// out because the compiler folds the builtin's two results into one when both
+// operands are the same value.  s_nop 1 covers the VALU-write -> permlane-read
+// hazard.
+template <int G>
+__device__ __forceinline__ float sum_state_groups(float v) {
+  if constexpr (G == 1) {
+    return v;
+  } else {
+    float a = v, b = v;
+    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+    float s = a + b;
+    if constexpr (G == 4) {
+      float c = s, d = s;
+      asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(c), "+v"(d));
+      s = c + d;
+    }
+    return s;
+  }
+}
+
+template <int S, int K>
+struct Unroll {
+  template <typename F>
+  static __device__ __forceinline__ void run(F&& f) {
+    f.template operator()<S>();
+    Unroll<S + 1, K>::run(f);
+  }
+};
+template <int K>
+struct Unroll<K, K> {
+  template <typename F>
+  static __device__ __forceinline__ void run(F&&) {}
+};
+
+inline bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (a == nullptr || b == nullptr || na == 0 || nb == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+inline bool aligned(const void* ptr, size_t a) { return (reinterpret_cast<uintptr_t>(ptr) % a) == 0; }
+
+}  // namespace

@@ -1,0 +1,800 @@
+// Backward of the fused selective-scan forward for MI355X (gfx950) and its C
+// ABI entry points.
+//
+// With the loss sum(dy * y) + sum(dh_last * h_last) and A = -exp(A_log), the
+// adjoint g_t of the state after step t obeys the reverse recurrence
+//     g_t = dh_last [t = last valid step] + dyp_t * C_t + Abar_{t+1} g_{t+1},
+// dyp_t = dy_t * silu(z_t) with the gate (else dy_t).  Written for mu_t, the
+// adjoint of the state before step t, it is the affine map
+//     mu_t = Abar_t * (dyp_t * C_t + mu_{t+1})
+// with per-step coefficients, so it composes over sub-chunks exactly like the
+// forward pair (Abar, b) and runs in reverse with the same fold / carry walk /
+// rescan structure as the forward kernel (the associative scan of the pwwt.cn
+// article, sections 2.1 and 3.1, applied to flipped time; the forward states it
+// needs are recomputed from the chunk-boundary states the forward saved, its
+// section 3.4).  Per step and state (g = mu_{t+1} + dyp_t C_t):
+//     dC[t,n] += dyp_t h_t            dB[t,n] += g Delta_t x_t    (sums over channels)
+//     dx_t = dyp_t D + Delta_t sum_n g B_t          dD += dyp_t x_t
+//     dDelta_t = x_t sum_n g B_t + sum_n g h_{t-1} Abar_t A
+//     dA[n] += g h_{t-1} Abar_t Delta_t,  dA_log = dA * A
+//     dDelta_raw = dDelta * [clip passes] * sigmoid(raw + bias),  dbias = sum dDelta_raw
+//     dz_t = dy_t (C_t . h_t + D x_t) silu'(z_t),  dh0 = mu_0.
+//
+// Work mapping (one workgroup = one batch row x 16 channels, as in the
+// forward): a lane owns one channel, 16 states and K = 2 consecutive steps of
+// a tile; tiles are visited from the last to the first and the adjoint carry
+// stays in a register from tile to tile.  Per tile:
+//  * pass 1: Delta, u = Delta x, Abar (cached, 2 x 16 VGPRs), the forward fold
+//    b_total and the reverse fold m = Abar_0 (c_0 + Abar_1 c_1), c = dyp C, to
+//    LDS;
+//  * walks (one lane per (channel, state)): the forward walk from the tile's
+//    saved start state leaves each sub-chunk's incoming state in LDS; the
+//    reverse walk from the adjoint carry leaves each sub-chunk's mu_{end+1};
+//  * pass 2: the lane rebuilds h over its K steps and runs the adjoint back
+//    over them, producing dx, dDelta_raw, dz, dA; the per-(step, state)
+//    contributions to dB and dC are summed over the 16 channels through LDS
+//    and written as one partial per channel group.
+// A second kernel sums the partials over channel groups (dB, dC) and over
+// batch rows (dA_log, dD, dbias) in a fixed order, so the result is
+// deterministic.
+//
+// All arithmetic is fp32.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstring>
+
+#include "ssm_internal.h"
+#include "ssm_scan.h"
+
+namespace {
+
+struct BwdParams {
+  const void* x;
+  const void* delta;
+  const float* A_log;
+  const void* B;
+  const void* C;
+  const float* D;
+  const int32_t* valid_len;
+  const float* h0;
+  const float* delta_bias;
+  const void* z;
+  const float* chunk_states;  // [nb, ceil(L / T), nd, N]: the state after every tile of T steps
+  const void* dy;
+  const float* dh_last;
+  void* dx;
+  void* ddelta;
+  void* dz;
+  float* dh0;
+  float* ws_dB;  // [n_cg, nb, L, N] partial sums over the 16 channels of a group
+  float* ws_dC;
+  float* ws_dA;  // [nb, nd, N]
+  float* ws_dD;  // [nb, nd]
+  float* ws_db;  // [nb, nd]
+  int64_t L;
+  int32_t nb;
+  int32_t nd;
+  int32_t n_cg;
+  int32_t clamp;
+  float dmin;
+  float dmax;
+};
+
+constexpr int kBwdK = 2;  // steps per lane and sub-chunk
+constexpr int kBwdW = 8;  // waves per workgroup
+
+template <int G>
+constexpr int64_t bwd_tile_g = kBwdW * (4 / G) * kBwdK;
+
+int64_t bwd_tile(int64_t N) {
+  switch (N) {
+    case 16:
+      return bwd_tile_g<1>;
+    case 32:
+      return bwd_tile_g<2>;
+    case 64:
+      return bwd_tile_g<4>;
+    default:
+      return 0;
+  }
+}
+
+__device__ __forceinline__ float sigmoid_f32(float v) { return __builtin_amdgcn_rcpf(1.0f + fast_exp2(-v * kLog2e)); }
+
+template <typename IO, int G, bool SOFTPLUS, bool CLAMP, bool GATE>
+__global__ __launch_bounds__(64 * kBwdW, 2) void ssm_bwd_kernel(BwdParams p) {
+  constexpr int K = kBwdK;
+  constexpr int W = kBwdW;
+  constexpr int N = 16 * G;
+  constexpr int QR = 4 / G;
+  constexpr int SUB = W * QR;  // sub-chunks per tile
+  constexpr int T = SUB * K;   // steps per tile
+  constexpr int NS = N + 4;
+  constexpr int SDS = SUB + 4;
+  constexpr int AGG = SUB * 16 * N;
+  constexpr int PAIRS = 16 * N;
+  constexpr int NT = 64 * W;
+  constexpr int PPL = (PAIRS + NT - 1) / NT;
+  constexpr int E = Elem<IO>::kBytes;
+  static_assert(SUB % 4 == 0, "sub-chunk records are read as quads");
+  static_assert(SUB * G == 32 && NT == 512, "one reducing thread per (16-lane row, state)");
+
+  // Sub-chunk records, float4 quads as in the forward: index
+  // ((j * N/4 + n/4) * 16 + c) * 4 + n%4.  agg_b: forward b_total, then the
+  // state entering the sub-chunk; agg_m: reverse fold m, then mu at the
+  // sub-chunk's end.  After pass 2 has read both, the two buffers stage the
+  // dB / dC contributions for the sums over channels.
+  __shared__ __attribute__((aligned(16))) float agg_b[AGG];
+  __shared__ __attribute__((aligned(16))) float agg_m[AGG];
+  __shared__ __attribute__((aligned(16))) float agg_sd[16 * SDS];
+  __shared__ __attribute__((aligned(16))) float a2s[16 * NS];
+  __shared__ float red[2][NT];  // end of kernel: dD and dbias per lane
+
+  const int64_t total = static_cast<int64_t>(p.nb) * p.n_cg;
+  const int64_t bid = blockIdx.x;
+  const int64_t per_xcd = total / 8;
+  const int64_t logical = (bid < per_xcd * 8) ? (bid % 8) * per_xcd + bid / 8 : bid;
+  const int b = static_cast<int>(logical / p.n_cg);
+  const int cg = static_cast<int>(logical % p.n_cg);
+
+  const int tid = threadIdx.x;
+  const int w = tid >> 6;
+  const int lane = tid & 63;
+  const int r = lane >> 4;
+  const int c = lane & 15;
+  const int q = r / G;
+  const int g = r % G;
+  const int j = w * QR + q;
+  const int d = cg * 16 + c;
+  const int nd = p.nd;
+  const int64_t L = p.L;
+  int64_t len = L;
+  if (p.valid_len != nullptr) {
+    const int64_t v = p.valid_len[b];
+    len = v < 0 ? 0 : (v > L ? L : v);
+  }
+
+  for (int k = tid; k < 16 * N; k += NT) {
+    const int cc = k / N, n = k % N;
+    a2s[cc * NS + n] = -expf(p.A_log[static_cast<int64_t>(cg * 16 + cc) * N + n]) * kLog2e;
+  }
+  const float dskip = (p.D != nullptr) ? p.D[d] : 0.0f;
+  const float dbias = (p.delta_bias != nullptr) ? p.delta_bias[d] : 0.0f;
+
+  auto pair_of = [&](int k, int& cc, int& n) {
+    const int pr = tid + k * NT;
+    cc = pr % 16;
+    n = pr / 16;
+  };
+  auto pair_valid = [&](int k) { return PAIRS % NT == 0 || tid + k * NT < PAIRS; };
+  auto pair_offset = [&](int k) {
+    int cc, n;
+    pair_of(k, cc, n);
+    return static_cast<uint32_t>(cc * N + n);
+  };
+  const int64_t state_block = (static_cast<int64_t>(b) * nd + cg * 16) * N;
+  const int64_t n_tiles = (L + T - 1) / T;
+
+  // The adjoint carry (mu entering the current tile from the future) and the
+  // per-pair dA accumulator, held by the walk lanes.
+  float mu_carry[PPL], dA_acc[PPL];
+#pragma unroll
+  for (int k = 0; k < PPL; ++k) {
+    mu_carry[k] = (p.dh_last != nullptr && pair_valid(k)) ? p.dh_last[state_block + pair_offset(k)] : 0.0f;
+    dA_acc[k] = 0.0f;
+  }
+  float dD_acc = 0.0f, db_acc = 0.0f;  // this lane's steps, channel d (counted once per (t, d))
+
+  const int64_t xd_step = static_cast<int64_t>(nd) * E;
+  const int64_t bc_step = static_cast<int64_t>(N) * E;
+  const int64_t xd_row = L * xd_step, bc_row = L * bc_step;
+  const rsrc_t rx = make_rsrc(static_cast<const char*>(p.x) + b * xd_row, xd_row);
+  const rsrc_t rd = make_rsrc(static_cast<const char*>(p.delta) + b * xd_row, xd_row);
+  const rsrc_t rdy = make_rsrc(static_cast<const char*>(p.dy) + b * xd_row, xd_row);
+  const rsrc_t rz = make_rsrc(GATE ? static_cast<const char*>(p.z) + b * xd_row : nullptr, GATE ? xd_row : 0);
+  const rsrc_t rdx = make_rsrc(static_cast<char*>(p.dx) + b * xd_row, xd_row);
+  const rsrc_t rdd = make_rsrc(static_cast<char*>(p.ddelta) + b * xd_row, xd_row);
+  const rsrc_t rdz = make_rsrc(GATE ? static_cast<char*>(p.dz) + b * xd_row : nullptr, GATE ? xd_row : 0);
+  const rsrc_t rb = make_rsrc(static_cast<const char*>(p.B) + b * bc_row, bc_row);
+  const rsrc_t rc = make_rsrc(static_cast<const char*>(p.C) + b * bc_row, bc_row);
+  const uint32_t off_xd = static_cast<uint32_t>((j * K * nd + d) * E);
+  const uint32_t off_bc = static_cast<uint32_t>((j * K * N + 16 * g + c) * E);
+  // dB / dC partials of this channel group: [n_cg, nb, L, N]
+  float* const wdB = p.ws_dB + ((static_cast<int64_t>(cg) * p.nb + b) * L) * N;
+  float* const wdC = p.ws_dC + ((static_cast<int64_t>(cg) * p.nb + b) * L) * N;
+
+  __syncthreads();  // a2s is written
+
+  for (int64_t kt = n_tiles - 1; kt >= 0; --kt) {
+    const int64_t t_tile = kt * T;
+    const int64_t left = len - t_tile - j * K;  // valid steps from this lane's first step
+    if (len <= t_tile) {
+      // A tile wholly in the padding: zero gradients, the adjoint passes through.
+#pragma unroll
+      for (int i = 0; i < K; ++i) {
+        if (j * K + i < L - t_tile && (G == 1 || (i % G) == g)) {
+          const uint32_t sx = static_cast<uint32_t>((t_tile + i) * xd_step);
+          Elem<IO>::store(rdx, off_xd, sx, 0.0f);
+          Elem<IO>::store(rdd, off_xd, sx, 0.0f);
+          if constexpr (GATE) Elem<IO>::store(rdz, off_xd, sx, 0.0f);
+        }
+      }
+      continue;
+    }
+
+    // ---- loads ----
+    float xv[K], dlr[K], dyv[K], zv[K], bv[K], cv[K];
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      const bool ok = i < left;
+      const uint32_t sx = static_cast<uint32_t>((t_tile + i) * xd_step);
+      const uint32_t sb = static_cast<uint32_t>((t_tile + i) * bc_step);
+      xv[i] = ok ? Elem<IO>::template load<kStream>(rx, off_xd, sx) : 0.0f;
+      dlr[i] = ok ? Elem<IO>::template load<kStream>(rd, off_xd, sx) : 0.0f;
+      dyv[i] = ok ? Elem<IO>::template load<kStream>(rdy, off_xd, sx) : 0.0f;
+      zv[i] = (GATE && ok) ? Elem<IO>::template load<kStream>(rz, off_xd, sx) : 0.0f;
+      bv[i] = ok ? Elem<IO>::template load<0>(rb, off_bc, sb) : 0.0f;
+      cv[i] = ok ? Elem<IO>::template load<0>(rc, off_bc, sb) : 0.0f;
+    }
+    float A2[16];
+    {
+      const float* pa = a2s + c * NS + 16 * g;
+#pragma unroll
+      for (int s = 0; s < 16; s += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(pa + s);
+        A2[s] = v.x;
+        A2[s + 1] = v.y;
+        A2[s + 2] = v.z;
+        A2[s + 3] = v.w;
+      }
+    }
+
+    // ---- pass 1 ----
+    float dl[K], fac[K], u[K], dyp[K], sg_z[K];
+    float sd = 0.0f;
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      const bool ok = i < left;
+      const float raw = dlr[i] + dbias;
+      float v = raw, f = 1.0f;
+      if constexpr (SOFTPLUS) {
+        v = softplus_f32(raw);
+        f = sigmoid_f32(raw);
+      }
+      if constexpr (CLAMP) {
+        f = (v >= p.dmin && v <= p.dmax) ? f : 0.0f;
+        v = __builtin_amdgcn_fmed3f(v, p.dmin, p.dmax);
+      }
+      dl[i] = ok ? v : 0.0f;
+      fac[i] = ok ? f : 0.0f;
+      u[i] = dl[i] * xv[i];
+      sd += dl[i];
+      if constexpr (GATE) {
+        sg_z[i] = sigmoid_f32(zv[i]);
+        dyp[i] = dyv[i] * zv[i] * sg_z[i];
+      } else {
+        sg_z[i] = 0.0f;
+        dyp[i] = dyv[i];
+      }
+    }
+    float ab[K][16];
+    float bt[16], mm[16];
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      const float bi = bv[i];
+      const float ui = u[i];
+      Unroll<0, 16>::run([&]<int S>() {
+        ab[i][S] = fast_exp2(dl[i] * A2[S]);
+        bt[S] = (i == 0) ? row_bcast<S>(bi) * ui : __builtin_fmaf(ab[i][S], bt[S], row_bcast<S>(bi) * ui);
+      });
+    }
+    {
+      // reverse fold over the K = 2 steps: m = Abar_0 (c_0 + Abar_1 c_1)
+      const float c0 = cv[0], c1 = cv[1], y0 = dyp[0], y1 = dyp[1];
+      Unroll<0, 16>::run([&]<int S>() {
+        const float t1 = ab[1][S] * (row_bcast<S>(c1) * y1);
+        mm[S] = ab[0][S] * __builtin_fmaf(row_bcast<S>(c0), y0, t1);
+      });
+    }
+    {
+      float* pb = agg_b + ((j * (N / 4) + 4 * g) * 16 + c) * 4;
+      float* pm = agg_m + ((j * (N / 4) + 4 * g) * 16 + c) * 4;
+#pragma unroll
+      for (int s = 0; s < 16; s += 4) {
+        *reinterpret_cast<float4*>(pb + s * 16) = make_float4(bt[s], bt[s + 1], bt[s + 2], bt[s + 3]);
+        *reinterpret_cast<float4*>(pm + s * 16) = make_float4(mm[s], mm[s + 1], mm[s + 2], mm[s + 3]);
+      }
+      if (g == 0) agg_sd[c * SDS + j] = sd;
+    }
+    __syncthreads();
+
+    // ---- walks: forward states into the sub-chunks, adjoints out of them ----
+#pragma unroll
+    for (int k = 0; k < PPL; ++k) {
+      if (pair_valid(k)) {
+        int cc, n;
+        pair_of(k, cc, n);
+        const float a2 = a2s[cc * NS + n];
+        float* pbw = agg_b + ((n / 4) * 16 + cc) * 4 + (n % 4);
+        float* pmw = agg_m + ((n / 4) * 16 + cc) * 4 + (n % 4);
+        const float* psd = agg_sd + cc * SDS;
+        float av[SUB];
+#pragma unroll
+        for (int u4 = 0; u4 < SUB; u4 += 4) {
+          const float4 v = *reinterpret_cast<const float4*>(psd + u4);
+          av[u4] = fast_exp2(a2 * v.x);
+          av[u4 + 1] = fast_exp2(a2 * v.y);
+          av[u4 + 2] = fast_exp2(a2 * v.z);
+          av[u4 + 3] = fast_exp2(a2 * v.w);
+        }
+        float h;
+        if (kt == 0)
+          h = (p.h0 != nullptr) ? p.h0[state_block + pair_offset(k)] : 0.0f;
+        else
+          h = p.chunk_states[((static_cast<int64_t>(b) * n_tiles + kt - 1) * nd + cg * 16) * N + pair_offset(k)];
+#pragma unroll
+        for (int jj = 0; jj < SUB; ++jj) {
+          const float bb = pbw[jj * (N / 4) * 64];
+          pbw[jj * (N / 4) * 64] = h;
+          h = __builtin_fmaf(av[jj], h, bb);
+        }
+        float mu = mu_carry[k];
+#pragma unroll
+        for (int jj = SUB - 1; jj >= 0; --jj) {
+          const float m = pmw[jj * (N / 4) * 64];
+          pmw[jj * (N / 4) * 64] = mu;
+          mu = __builtin_fmaf(av[jj], mu, m);
+        }
+        mu_carry[k] = mu;
+      }
+    }
+    __syncthreads();
+
+    // ---- pass 2: rebuild h over the lane's steps, run the adjoint back ----
+    float hp[16], mu[16];
+    {
+      const float* pb = agg_b + ((j * (N / 4) + 4 * g) * 16 + c) * 4;
+      const float* pm = agg_m + ((j * (N / 4) + 4 * g) * 16 + c) * 4;
+#pragma unroll
+      for (int s = 0; s < 16; s += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(pb + s * 16);
+        hp[s] = v.x;
+        hp[s + 1] = v.y;
+        hp[s + 2] = v.z;
+        hp[s + 3] = v.w;
+        const float4 m = *reinterpret_cast<const float4*>(pm + s * 16);
+        mu[s] = m.x;
+        mu[s + 1] = m.y;
+        mu[s + 2] = m.z;
+        mu[s + 3] = m.w;
+      }
+    }
+    __syncthreads();  // agg_b / agg_m become the staging area below
+
+    float hm[16];  // state after step 0
+    {
+      float b0 = bv[0];
+      asm volatile("" : "+v"(b0));
+      const float u0 = u[0];
+      Unroll<0, 16>::run([&]<int S>() { hm[S] = __builtin_fmaf(ab[0][S], hp[S], row_bcast<S>(b0) * u0); });
+    }
+    float dAl[16];
+#pragma unroll
+    for (int s = 0; s < 16; ++s) dAl[s] = 0.0f;
+
+    // Staging for the sums over the 16 channels of a row: row block rb =
+    // j * G + g (32 of them) holds [s][c], so that the reducing thread of
+    // (rb, s) reads 16 consecutive floats.
+    const int rb = j * G + g;
+    auto reduce_stage = [&](int i) {
+      // thread (rb', s') sums the 16 channels of its row block for state s'
+      const int rr = tid >> 4, ss = tid & 15;
+      const float* pbs = agg_b + rr * 256 + ss * 16;
+      const float* pcs = agg_m + rr * 256 + ss * 16;
+      float sb = 0.0f, sc = 0.0f;
+#pragma unroll
+      for (int k4 = 0; k4 < 16; k4 += 4) {
+        const float4 vb = *reinterpret_cast<const float4*>(pbs + k4);
+        const float4 vc = *reinterpret_cast<const float4*>(pcs + k4);
+        sb += (vb.x + vb.y) + (vb.z + vb.w);
+        sc += (vc.x + vc.y) + (vc.z + vc.w);
+      }
+      const int jr = rr / G, gr = rr % G;
+      const int64_t t = t_tile + jr * K + i;
+      if (t < len) {
+        wdB[t * N + 16 * gr + ss] = sb;
+        wdC[t * N + 16 * gr + ss] = sc;
+      }
+    };
+
+#pragma unroll
+    for (int ii = 0; ii < K; ++ii) {
+      const int i = K - 1 - ii;  // steps in reverse
+      // the state after step i and the one before it
+      float hn[16];
+      if (i == 1) {
+        float b1 = bv[1];
+        asm volatile("" : "+v"(b1));
+        const float u1 = u[1];
+        Unroll<0, 16>::run([&]<int S>() { hn[S] = __builtin_fmaf(ab[1][S], hm[S], row_bcast<S>(b1) * u1); });
+      } else {
+#pragma unroll
+        for (int s = 0; s < 16; ++s) hn[s] = hm[s];
+      }
+      const float(&hb)[16] = (i == 1) ? hm : hp;  // state before step i
+      float ci = cv[i];
+      float bi = bv[i];
+      asm volatile("" : "+v"(ci), "+v"(bi));
+      const float yi = dyp[i];
+      float sgb = 0.0f, sda = 0.0f, ypre = 0.0f;
+      float* pbs = agg_b + rb * 256 + c;
+      float* pcs = agg_m + rb * 256 + c;
+      Unroll<0, 16>::run([&]<int S>() {
+        const float gg = __builtin_fmaf(row_bcast<S>(ci), yi, mu[S]);  // adjoint of the state after step i
+        sgb = __builtin_fmaf(gg, row_bcast<S>(bi), sgb);
+        const float daa = gg * hb[S] * ab[i][S];
+        sda = __builtin_fmaf(daa, A2[S], sda);
+        dAl[S] = __builtin_fmaf(daa, dl[i], dAl[S]);
+        if constexpr (GATE) ypre = __builtin_fmaf(row_bcast<S>(ci), hn[S], ypre);
+        pbs[S * 16] = gg * u[i];
+        pcs[S * 16] = yi * hn[S];
+        mu[S] = ab[i][S] * gg;
+      });
+      sgb = sum_state_groups<G>(sgb);
+      sda = sum_state_groups<G>(sda);
+      if constexpr (GATE) ypre = sum_state_groups<G>(ypre) + dskip * xv[i];
+      const float ddt = __builtin_fmaf(xv[i], sgb, sda * kLn2);  // A = A2 ln 2
+      const float ddraw = ddt * fac[i];
+      const float dxv = __builtin_fmaf(dl[i], sgb, yi * dskip);
+      if (i < left && (G == 1 || (i % G) == g)) {
+        const uint32_t sx = static_cast<uint32_t>((t_tile + i) * xd_step);
+        Elem<IO>::store(rdx, off_xd, sx, dxv);
+        Elem<IO>::store(rdd, off_xd, sx, ddraw);
+        if constexpr (GATE) {
+          const float sz = sg_z[i];
+          Elem<IO>::store(rdz, off_xd, sx, dyv[i] * ypre * sz * __builtin_fmaf(zv[i], 1.0f - sz, 1.0f));
+        }
+        dD_acc = __builtin_fmaf(yi, xv[i], dD_acc);
+        db_acc += ddraw;
+      } else if (j * K + i < L - t_tile && (G == 1 || (i % G) == g)) {
+        const uint32_t sx = static_cast<uint32_t>((t_tile + i) * xd_step);
+        Elem<IO>::store(rdx, off_xd, sx, 0.0f);
+        Elem<IO>::store(rdd, off_xd, sx, 0.0f);
+        if constexpr (GATE) Elem<IO>::store(rdz, off_xd, sx, 0.0f);
+      }
+      __syncthreads();
+      reduce_stage(i);
+      __syncthreads();
+    }
+
+    // dA: the lane's two steps, summed over the sub-chunks of the tile by the
+    // walk lanes (staged [state][channel][j] through agg_b: 16 N rows of SUB).
+#pragma unroll
+    for (int s = 0; s < 16; ++s) agg_b[((16 * g + s) * 16 + c) * SUB + j] = dAl[s];
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < PPL; ++k) {
+      if (pair_valid(k)) {
+        int cc, n;
+        pair_of(k, cc, n);
+        const float* pa = agg_b + (n * 16 + cc) * SUB;
+        float s4 = 0.0f;
+#pragma unroll
+        for (int u4 = 0; u4 < SUB; u4 += 4) {
+          const float4 v = *reinterpret_cast<const float4*>(pa + u4);
+          s4 += (v.x + v.y) + (v.z + v.w);
+        }
+        dA_acc[k] += s4;
+      }
+    }
+    __syncthreads();  // the next tile's pass 1 overwrites agg_b
+  }
+
+  // ---- per-(b, d) and per-(b, d, n) results ----
+#pragma unroll
+  for (int k = 0; k < PPL; ++k) {
+    if (pair_valid(k)) {
+      int cc, n;
+      pair_of(k, cc, n);
+      const int64_t o = state_block + pair_offset(k);
+      if (p.dh0 != nullptr) p.dh0[o] = mu_carry[k];
+      p.ws_dA[o] = dA_acc[k];
+    }
+  }
+  red[0][tid] = dD_acc;
+  red[1][tid] = db_acc;
+  __syncthreads();
+  if (tid < 16) {
+    // lanes of channel tid: lane index (w, r, c = tid) over all waves and rows
+    float s0 = 0.0f, s1 = 0.0f;
+    for (int ww = 0; ww < W; ++ww)
+      for (int rr = 0; rr < 4; ++rr) {
+        s0 += red[0][ww * 64 + rr * 16 + tid];
+        s1 += red[1][ww * 64 + rr * 16 + tid];
+      }
+    p.ws_dD[static_cast<int64_t>(b) * nd + cg * 16 + tid] = s0;
+    p.ws_db[static_cast<int64_t>(b) * nd + cg * 16 + tid] = s1;
+  }
+}
+
+// Sums the partials in a fixed order: dB, dC over channel groups (zero past
+// each row's valid length), dA_log = A * sum over rows of dA, dD and dbias
+// over rows.
+struct ReduceParams {
+  const float* ws_dB;
+  const float* ws_dC;
+  const float* ws_dA;
+  const float* ws_dD;
+  const float* ws_db;
+  const float* A_log;
+  const int32_t* valid_len;
+  float* dB;
+  float* dC;
+  float* dA_log;
+  float* dD;
+  float* dbias;
+  int64_t L;
+  int32_t nb, nd, N, n_cg;
+};
+
+__global__ __launch_bounds__(256) void ssm_bwd_reduce_kernel(ReduceParams p) {
+  const int64_t n_bc = static_cast<int64_t>(p.nb) * p.L * p.N;
+  const int64_t n_dn = static_cast<int64_t>(p.nd) * p.N;
+  const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n_bc + n_dn + p.nd;
+       i += stride) {
+    if (i < n_bc) {
+      const int64_t b = i / (p.L * p.N), t = (i / p.N) % p.L;
+      int64_t len = p.L;
+      if (p.valid_len != nullptr) {
+        const int64_t v = p.valid_len[b];
+        len = v < 0 ? 0 : (v > p.L ? p.L : v);
+      }
+      float sb = 0.0f, sc = 0.0f;
+      if (t < len) {
+        for (int g = 0; g < p.n_cg; ++g) {
+          sb += p.ws_dB[g * n_bc + i];
+          sc += p.ws_dC[g * n_bc + i];
+        }
+      }
+      p.dB[i] = sb;
+      p.dC[i] = sc;
+    } else if (i < n_bc + n_dn) {
+      const int64_t k = i - n_bc;
+      float s = 0.0f;
+      for (int b = 0; b < p.nb; ++b) s += p.ws_dA[b * n_dn + k];
+      p.dA_log[k] = s * -expf(p.A_log[k]);
+    } else {
+      const int64_t dd = i - n_bc - n_dn;
+      float s0 = 0.0f, s1 = 0.0f;
+      for (int b = 0; b < p.nb; ++b) {
+        s0 += p.ws_dD[b * p.nd + dd];
+        s1 += p.ws_db[b * p.nd + dd];
+      }
+      if (p.dD != nullptr) p.dD[dd] = s0;
+      if (p.dbias != nullptr) p.dbias[dd] = s1;
+    }
+  }
+}
+
+template <typename IO, int G, bool SP, bool CL, bool GATE>
+hipError_t bwd_launch_flags(const BwdParams& prm, hipStream_t stream) {
+  const int64_t blocks = static_cast<int64_t>(prm.nb) * prm.n_cg;
+  hipLaunchKernelGGL((ssm_bwd_kernel<IO, G, SP, CL, GATE>), dim3(static_cast<unsigned>(blocks)), dim3(64 * kBwdW),
+                     0, stream, prm);
+  return hipGetLastError();
+}
+
+template <typename IO, int G>
+hipError_t bwd_launch(const BwdParams& prm, bool sp, hipStream_t stream) {
+  const bool gate = prm.z != nullptr;
+  if (sp) {
+    if (prm.clamp)
+      return gate ? bwd_launch_flags<IO, G, true, true, true>(prm, stream)
+                  : bwd_launch_flags<IO, G, true, true, false>(prm, stream);
+    return gate ? bwd_launch_flags<IO, G, true, false, true>(prm, stream)
+                : bwd_launch_flags<IO, G, true, false, false>(prm, stream);
+  }
+  if (prm.clamp)
+    return gate ? bwd_launch_flags<IO, G, false, true, true>(prm, stream)
+                : bwd_launch_flags<IO, G, false, true, false>(prm, stream);
+  return gate ? bwd_launch_flags<IO, G, false, false, true>(prm, stream)
+              : bwd_launch_flags<IO, G, false, false, false>(prm, stream);
+}
+
+template <typename IO>
+hipError_t bwd_launch_io(int G, const BwdParams& prm, bool sp, hipStream_t stream) {
+  switch (G) {
+    case 1:
+      return bwd_launch<IO, 1>(prm, sp, stream);
+    case 2:
+      return bwd_launch<IO, 2>(prm, sp, stream);
+    default:
+      return bwd_launch<IO, 4>(prm, sp, stream);
+  }
+}
+
+// Workspace floats: dB and dC partials per channel group, dA per row, dD and
+// dbias per row.
+int64_t bwd_ws_floats(int64_t nb, int64_t L, int64_t nd, int64_t N) {
+  return 2 * (nd / 16) * nb * L * N + nb * nd * N + 2 * nb * nd;
+}
+
+__global__ void zero_fill_kernel(float* dst, int64_t n) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = 0.0f;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t ssm_scan_bwd_chunk_len(int64_t dstate) { return bwd_tile(dstate); }
+
+int64_t ssm_scan_bwd_workspace_bytes(const ssm_scan_dims* dims) {
+  if (dims == nullptr || dims->batch < 0 || dims->seqlen < 0 || dims->dim < 0) return -1;
+  if (bwd_tile(dims->dstate) == 0 || dims->dim % 16 != 0) return -1;
+  return 4 * bwd_ws_floats(dims->batch, dims->seqlen, dims->dim, dims->dstate);
+}
+
+// Checks run in this order: dims and flags; pointers; alignment; aliasing;
+// the handle; the current device.  Nothing is enqueued unless all pass.
+int ssm_selective_scan_bwd(ssm_scan_t handle, const void* x, const void* delta, const float* A_log, const void* B,
+                           const void* C, const float* D, const int32_t* valid_len, const ssm_scan_dims* dims,
+                           const ssm_scan_fwd_extras* extras, const ssm_scan_bwd_io* io, void* stream) {
+  if (dims == nullptr || io == nullptr) return SSM_ERR_INVALID_ARG;
+  const int64_t nb = dims->batch, L = dims->seqlen, nd = dims->dim, N = dims->dstate;
+  if (nb < 0 || L < 0 || nd < 0 || N < 0) return SSM_ERR_INVALID_ARG;
+  if (dims->io_dtype != SSM_IO_F32 && dims->io_dtype != SSM_IO_BF16) return SSM_ERR_INVALID_ARG;
+  if (dims->delta_softplus != 0 && dims->delta_softplus != 1) return SSM_ERR_INVALID_ARG;
+  if (dims->delta_clamp != 0 && dims->delta_clamp != 1) return SSM_ERR_INVALID_ARG;
+  if (dims->delta_clamp == 1 && !(dims->delta_min >= 0.0f && dims->delta_min <= dims->delta_max &&
+                                  dims->delta_max < __builtin_inff()))
+    return SSM_ERR_INVALID_ARG;
+  if (N != 16 && N != 32 && N != 64) return SSM_ERR_UNSUPPORTED;
+  if (nd % 16 != 0) return SSM_ERR_UNSUPPORTED;
+  if (nb > 0 && nd > 0 && (nb * (nd / 16) > 0x7fffffffLL || nb > 0x7fffffffLL || nd > 0x7fffffffLL))
+    return SSM_ERR_UNSUPPORTED;
+  const int64_t esz = dims->io_dtype == SSM_IO_BF16 ? 2 : 4;
+  if (L > 0 && L * (N > nd ? N : nd) * esz > 0x7fffffffLL) return SSM_ERR_UNSUPPORTED;
+  const ssm_scan_fwd_extras none = {nullptr, nullptr, nullptr, nullptr, 0, 0, nullptr, 0};
+  const ssm_scan_fwd_extras& ex = extras ? *extras : none;
+  const int64_t T = bwd_tile(N);
+  const int64_t n_tiles = L > 0 ? (L + T - 1) / T : 0;
+  const int64_t need = 4 * bwd_ws_floats(nb, L, nd, N);
+  if (io->workspace_bytes < need) return SSM_ERR_INVALID_ARG;
+
+  const bool empty = (nb == 0 || nd == 0);
+  const size_t e = static_cast<size_t>(esz);
+  const size_t n_xd = static_cast<size_t>(nb) * L * nd, n_bc = static_cast<size_t>(nb) * L * N;
+  const size_t n_state = static_cast<size_t>(nb) * nd * N;
+  if (!empty) {
+    if (A_log == nullptr || io->dA_log == nullptr || io->workspace == nullptr) return SSM_ERR_INVALID_ARG;
+    if (L > 0 && (x == nullptr || delta == nullptr || B == nullptr || C == nullptr || io->dy == nullptr ||
+                  io->dx == nullptr || io->ddelta == nullptr || io->dB == nullptr || io->dC == nullptr))
+      return SSM_ERR_INVALID_ARG;
+    if (L > 0 && n_tiles > 1 && io->chunk_states == nullptr) return SSM_ERR_INVALID_ARG;
+    if (L > 0 && ex.z != nullptr && io->dz == nullptr) return SSM_ERR_INVALID_ARG;
+    const void* es[] = {x, delta, B, C, ex.z, io->dy, io->dx, io->ddelta, io->dz};
+    for (const void* q : es)
+      if (!aligned(q, e)) return SSM_ERR_UNSUPPORTED;
+    const void* fs[] = {A_log, D, valid_len, ex.h0, ex.delta_bias, io->dh_last, io->chunk_states, io->dA_log,
+                        io->dB, io->dC, io->dD, io->ddelta_bias, io->dh0, io->workspace};
+    for (const void* q : fs)
+      if (!aligned(q, 4)) return SSM_ERR_UNSUPPORTED;
+    const size_t bxd = L > 0 ? n_xd * e : 0;
+    const size_t bcs = static_cast<size_t>(n_tiles > 1 ? n_tiles - 1 : 0) * n_state * 4;
+    const void* ins[] = {x, delta, B, C, A_log, D, valid_len, L > 0 ? ex.z : nullptr, ex.h0, ex.delta_bias,
+                         L > 0 ? io->dy : nullptr, io->dh_last, io->chunk_states};
+    const size_t ins_n[] = {n_xd * e, n_xd * e, n_bc * e, n_bc * e, static_cast<size_t>(nd) * N * 4,
+                            D ? static_cast<size_t>(nd) * 4 : 0, valid_len ? static_cast<size_t>(nb) * 4 : 0,
+                            ex.z ? n_xd * e : 0, ex.h0 ? n_state * 4 : 0, ex.delta_bias ? static_cast<size_t>(nd) * 4 : 0,
+                            bxd, io->dh_last ? n_state * 4 : 0, io->chunk_states ? bcs : 0};
+    void* outs[] = {io->dx, io->ddelta, io->dz, io->dA_log, io->dB, io->dC, io->dD, io->ddelta_bias, io->dh0,
+                    io->workspace};
+    const size_t outs_n[] = {bxd, bxd, ex.z ? bxd : 0, static_cast<size_t>(nd) * N * 4, L > 0 ? n_bc * 4 : 0,
+                             L > 0 ? n_bc * 4 : 0, io->dD ? static_cast<size_t>(nd) * 4 : 0,
+                             io->ddelta_bias ? static_cast<size_t>(nd) * 4 : 0, io->dh0 ? n_state * 4 : 0,
+                             static_cast<size_t>(need)};
+    for (int o = 0; o < 10; ++o) {
+      for (int k = 0; k < 13; ++k)
+        if (overlaps(outs[o], outs_n[o], ins[k], ins_n[k])) return SSM_ERR_ALIAS;
+      for (int o2 = o + 1; o2 < 10; ++o2)
+        if (overlaps(outs[o], outs_n[o], outs[o2], outs_n[o2])) return SSM_ERR_ALIAS;
+    }
+  }
+  if (handle == nullptr) return SSM_ERR_INVALID_ARG;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) {
+    (void)hipGetLastError();
+    return SSM_ERR_HIP;
+  }
+  if (cur != handle->device) return SSM_ERR_DEVICE_MISMATCH;
+  if (empty) return SSM_OK;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* ws = static_cast<float*>(io->workspace);
+  const int64_t n_cg = nd / 16;
+  BwdParams prm;
+  prm.x = x;
+  prm.delta = delta;
+  prm.A_log = A_log;
+  prm.B = B;
+  prm.C = C;
+  prm.D = D;
+  prm.valid_len = valid_len;
+  prm.h0 = ex.h0;
+  prm.delta_bias = ex.delta_bias;
+  prm.z = ex.z;
+  prm.chunk_states = io->chunk_states;
+  prm.dy = io->dy;
+  prm.dh_last = io->dh_last;
+  prm.dx = io->dx;
+  prm.ddelta = io->ddelta;
+  prm.dz = ex.z != nullptr ? io->dz : nullptr;
+  prm.dh0 = io->dh0;
+  prm.ws_dB = ws;
+  prm.ws_dC = ws + n_cg * nb * L * N;
+  prm.ws_dA = ws + 2 * n_cg * nb * L * N;
+  prm.ws_dD = prm.ws_dA + nb * nd * N;
+  prm.ws_db = prm.ws_dD + nb * nd;
+  prm.L = L;
+  prm.nb = static_cast<int32_t>(nb);
+  prm.nd = static_cast<int32_t>(nd);
+  prm.n_cg = static_cast<int32_t>(n_cg);
+  prm.clamp = dims->delta_clamp;
+  prm.dmin = dims->delta_min;
+  prm.dmax = dims->delta_max;
+  const int G = static_cast<int>(N / 16);
+  if (L == 0) {
+    // No steps: the adjoint of the initial state is dh_last; every other
+    // gradient is zero.
+    const int64_t nz = nd * N + 2 * nd;
+    float* outs[] = {io->dA_log, io->dD, io->ddelta_bias};
+    const int64_t cnt[] = {nd * N, nd, nd};
+    (void)nz;
+    for (int k = 0; k < 3; ++k)
+      if (outs[k] != nullptr)
+        hipLaunchKernelGGL(zero_fill_kernel, dim3(static_cast<unsigned>((cnt[k] + 255) / 256)), dim3(256), 0, s,
+                           outs[k], cnt[k]);
+    if (io->dh0 != nullptr) {
+      const int64_t n = nb * nd * N;
+      if (io->dh_last != nullptr)
+        (void)hipMemcpyAsync(io->dh0, io->dh_last, static_cast<size_t>(n) * 4, hipMemcpyDeviceToDevice, s);
+      else
+        hipLaunchKernelGGL(zero_fill_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, io->dh0,
+                           n);
+    }
+    return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+  }
+  hipError_t err = dims->io_dtype == SSM_IO_BF16 ? bwd_launch_io<uint16_t>(G, prm, dims->delta_softplus != 0, s)
+                                                 : bwd_launch_io<float>(G, prm, dims->delta_softplus != 0, s);
+  if (err != hipSuccess) return SSM_ERR_HIP;
+  ReduceParams rp;
+  rp.ws_dB = prm.ws_dB;
+  rp.ws_dC = prm.ws_dC;
+  rp.ws_dA = prm.ws_dA;
+  rp.ws_dD = prm.ws_dD;
+  rp.ws_db = prm.ws_db;
+  rp.A_log = A_log;
+  rp.valid_len = valid_len;
+  rp.dB = io->dB;
+  rp.dC = io->dC;
+  rp.dA_log = io->dA_log;
+  rp.dD = io->dD;
+  rp.dbias = io->ddelta_bias;
+  rp.L = L;
+  rp.nb = static_cast<int32_t>(nb);
+  rp.nd = static_cast<int32_t>(nd);
+  rp.N = static_cast<int32_t>(N);
+  rp.n_cg = static_cast<int32_t>(n_cg);
+  const int64_t work = nb * L * N + nd * N + nd;
+  int64_t blocks = (work + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(ssm_bwd_reduce_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s, rp);
+  return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
+}
+
+}  // extern "C"

@@ -163,6 +163,53 @@ def test_time_split_checks():
     assert _ex_call(d, E(time_parts=3, workspace=8 * MB, workspace_bytes=need)) == ssm.SSM_ERR_INVALID_ARG  # handle
 
 
+def test_bwd_checks():
+    import ctypes
+    BIO = ssm.ssm_scan_bwd_io
+    E = ssm.ssm_scan_fwd_extras
+    assert ssm.bwd_chunk_len(16) == 64 and ssm.bwd_chunk_len(32) == 32 and ssm.bwd_chunk_len(64) == 16
+    assert ssm.bwd_chunk_len(8) == 0
+    d = _dims(batch=2, seqlen=100, dim=32, dstate=16)
+    need = ssm.bwd_workspace_bytes(d)
+    assert need == 4 * (2 * 2 * 2 * 100 * 16 + 2 * 32 * 16 + 2 * 2 * 32)
+    assert ssm.bwd_workspace_bytes(_dims(dstate=8)) == -1 and ssm.bwd_workspace_bytes(_dims(dim=24)) == -1
+
+    def io(**kw):
+        base = dict(dy=8 * MB, chunk_states=9 * MB, dx=10 * MB, ddelta=11 * MB, dA_log=12 * MB, dB=13 * MB,
+                    dC=14 * MB, workspace=16 * MB, workspace_bytes=need)
+        base.update(kw)
+        return BIO(**base)
+
+    def call(bio, dims=d, extras=None, **over):
+        p = dict(PTRS, **over)
+        return ssm.ssm_selective_scan_bwd(None, p["x"], p["delta"], p["A_log"], p["B"], p["C"], p["D"],
+                                          p["valid_len"], dims, extras, bio, None)
+
+    assert call(io()) == ssm.SSM_ERR_INVALID_ARG  # everything valid: the NULL handle
+    bad_x = dict(x=PTRS["x"] + 1)
+    assert call(io(), **bad_x) == ssm.SSM_ERR_UNSUPPORTED  # misaligned input
+    assert call(io(workspace_bytes=need - 4), **bad_x) == ssm.SSM_ERR_INVALID_ARG  # workspace too small
+    assert call(io(workspace=None), **bad_x) == ssm.SSM_ERR_INVALID_ARG
+    assert call(io(chunk_states=None), **bad_x) == ssm.SSM_ERR_INVALID_ARG  # 100 steps > one 64-step tile
+    assert call(io(chunk_states=None), dims=_dims(batch=2, seqlen=64, dim=32, dstate=16), **bad_x) == \
+        ssm.SSM_ERR_UNSUPPORTED  # one tile needs no chunk states
+    for k in ("dy", "dx", "ddelta", "dA_log", "dB", "dC"):
+        assert call(io(**{k: None}), **bad_x) == ssm.SSM_ERR_INVALID_ARG, k
+    # the gate needs dz
+    assert call(io(), extras=E(z=15 * MB), **bad_x) == ssm.SSM_ERR_INVALID_ARG
+    assert call(io(dz=17 * MB), extras=E(z=15 * MB), **bad_x) == ssm.SSM_ERR_UNSUPPORTED
+    # outputs may not overlap inputs, each other or the workspace
+    assert call(io(dx=PTRS["x"])) == ssm.SSM_ERR_ALIAS
+    assert call(io(dB=8 * MB)) == ssm.SSM_ERR_ALIAS  # dy
+    assert call(io(dC=13 * MB + 64)) == ssm.SSM_ERR_ALIAS  # dB
+    assert call(io(workspace=12 * MB)) == ssm.SSM_ERR_ALIAS  # dA_log
+    assert call(io(dh0=9 * MB)) == ssm.SSM_ERR_ALIAS  # chunk states
+    assert call(io(dD=11 * MB + 2)) == ssm.SSM_ERR_UNSUPPORTED  # misaligned
+    assert ssm.ssm_selective_scan_bwd(None, *[None] * 7, d, None, io(), None) == ssm.SSM_ERR_INVALID_ARG
+    assert ssm.ssm_selective_scan_bwd(None, *[None] * 7, _dims(dstate=8), None, io(), None) == \
+        ssm.SSM_ERR_UNSUPPORTED
+
+
 def test_empty_problem_needs_only_the_handle():
     assert call(_dims(batch=0), x=None, delta=None, B=None, C=None, y=None, A_log=None) == ssm.SSM_ERR_INVALID_ARG
 

@@ -1,0 +1,122 @@
+"""The backward on the GPU against the fp64 oracle's backward (which the CPU
+suite pins to finite differences and exact identities)."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+from conftest import rel_err
+from gpu_util import to_device, to_np64
+from selective_state_space_scan_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+GRADS = ("dx", "ddelta", "dA_log", "dB", "dC", "dD", "ddelta_bias", "dz", "dh0")
+
+
+def _case(io, N, L, nb, nd, seed, varlen=None, extras=True, clamp=None):
+    base = I.WORKLOADS[0] if io == "f32" else I.WORKLOADS[2]
+    w = dataclasses.replace(I.small_workload(base, batch=nb, seqlen=L, dim=nd), dstate=N)
+    inp = I.make_inputs(w, seed)
+    rng = np.random.default_rng(seed + 1)
+    rnd = (lambda a: I.round_to_bf16(a)) if io == "bf16" else (lambda a: a.astype(np.float32))
+    inp["dy"] = rnd(rng.standard_normal((nb, L, nd)).astype(np.float32))
+    inp["dh_last"] = rng.standard_normal((nb, nd, N)).astype(np.float32)
+    if extras:
+        inp["h0"] = rng.standard_normal((nb, nd, N)).astype(np.float32)
+        inp["delta_bias"] = (0.5 * rng.standard_normal(nd)).astype(np.float32)
+        inp["z"] = rnd(2.0 * rng.standard_normal((nb, L, nd)).astype(np.float32))
+    if varlen is not None:
+        inp["valid_len"] = np.asarray(varlen, dtype=np.int32)
+    return w, inp
+
+
+def _gpu(inp, io, clamp=None, time_parts=None):
+    import torch
+    import selective_state_space_scan_amd as ssm
+    dev = to_device(inp, io)
+    dt = dev["x"].dtype
+    ex = {}
+    if "h0" in inp:
+        ex = dict(h0=torch.from_numpy(inp["h0"]).cuda(), delta_bias=torch.from_numpy(inp["delta_bias"]).cuda(),
+                  z=torch.from_numpy(inp["z"]).cuda().to(dt))
+    N = dev["A_log"].shape[1]
+    y, h, cs = ssm.selective_scan_fwd(dev["x"], dev["delta"], dev["A_log"], dev["B"], dev["C"], dev["D"],
+                                      dev["valid_len"], delta_clamp=clamp, return_chunk_states=True,
+                                      chunk_len=ssm.bwd_chunk_len(N), time_parts=time_parts, **ex)
+    dy = torch.from_numpy(inp["dy"]).cuda().to(dt)
+    dhl = torch.from_numpy(inp["dh_last"]).cuda()
+    g = ssm.selective_scan_bwd(dev["x"], dev["delta"], dev["A_log"], dev["B"], dev["C"], dev["D"], dev["valid_len"],
+                               dy, cs, dh_last=dhl, delta_clamp=clamp, **ex)
+    torch.cuda.synchronize()
+    return g
+
+
+def _oracle(inp, clamp=None):
+    import oracle
+    return oracle.selective_scan_bwd(inp["x"], inp["delta"], inp["A_log"], inp["B"], inp["C"], inp["D"], inp["dy"],
+                                     valid_len=inp.get("valid_len"), h0=inp.get("h0"),
+                                     delta_bias=inp.get("delta_bias"), z=inp.get("z"), dh_last=inp["dh_last"],
+                                     delta_clamp=clamp, nthreads=8)
+
+
+def _compare(g, r, tol, label):
+    worst = {}
+    for k in GRADS:
+        if r.get(k) is None or g.get(k) is None:
+            continue
+        worst[k] = rel_err(to_np64(g[k]), r[k])
+    print(label, " ".join(f"{k} {v:.1e}" for k, v in worst.items()), flush=True)
+    bad = {k: v for k, v in worst.items() if not v <= tol}
+    assert not bad, bad
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+@pytest.mark.parametrize("N", [16, 32, 64])
+def test_bwd_against_oracle(io, N):
+    import selective_state_space_scan_amd as ssm
+    T = ssm.bwd_chunk_len(N)
+    L = 7 * T + 13
+    w, inp = _case(io, N, L, 3, 32, seed=200 + N, varlen=[L, 3 * T + 5, 0])
+    g = _gpu(inp, io)
+    r = _oracle(inp)
+    _compare(g, r, 1e-4 if io == "f32" else 2e-2, f"{io} N={N}")
+    # padding: zero gradients past each row's length, the empty row's state adjoint passes through
+    assert np.all(to_np64(g["dx"][1, 3 * T + 5:]) == 0) and np.all(to_np64(g["dB"][2]) == 0)
+    assert np.array_equal(to_np64(g["dh0"][2]), inp["dh_last"][2].astype(np.float64))
+
+
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_bwd_plain_and_clamped(io):
+    """No extras (zero initial state, no bias, no gate), full rows; then the
+    long-workload recipe's clip on delta."""
+    w, inp = _case(io, 16, 300, 2, 48, seed=7, extras=False)
+    _compare(_gpu(inp, io), _oracle(inp), 1e-4 if io == "f32" else 2e-2, f"{io} plain")
+    w, inp = _case(io, 64, 200, 2, 32, seed=9, extras=False)
+    shifted = (inp["delta"] - 1.0).astype(np.float32)  # softplus values on both sides of the clip
+    inp["delta"] = I.round_to_bf16(shifted) if io == "bf16" else shifted
+    clamp = (1e-3, 0.01)
+    _compare(_gpu(inp, io, clamp=clamp), _oracle(inp, clamp=clamp), 1e-4 if io == "f32" else 2e-2, f"{io} clamp")
+
+
+def test_bwd_short_and_single_tile():
+    """Lengths below one tile and exactly one tile: no chunk states needed."""
+    import selective_state_space_scan_amd as ssm
+    for L in (1, 5, ssm.bwd_chunk_len(16)):
+        w, inp = _case("f32", 16, L, 2, 16, seed=L)
+        _compare(_gpu(inp, "f32"), _oracle(inp), 1e-4, f"L={L}")
+
+
+def test_bwd_deterministic():
+    w, inp = _case("bf16", 16, 500, 2, 64, seed=3)
+    a = _gpu(inp, "bf16")
+    b = _gpu(inp, "bf16")
+    for k in GRADS:
+        if a[k] is not None:
+            assert np.array_equal(a[k].cpu().float().numpy(), b[k].cpu().float().numpy()), k
+
+
+def test_bwd_after_time_split_forward():
+    """The chunk states of a time-split forward serve the backward equally."""
+    w, inp = _case("bf16", 64, 2048, 1, 32, seed=13)
+    _compare(_gpu(inp, "bf16", time_parts=4), _oracle(inp), 2e-2, "split fwd")
