@@ -12,6 +12,10 @@ Prints one JSON line on stdout: throughput in state updates per second
 (batch * L * dim * dstate per step, valid steps only for padded batches), the
 algorithmic HBM GB/s, a roofline object for the kernel, and the CPU oracle
 timed on this host on the same workload.
+
+``--pass bwd`` measures the backward instead (gradients of every input for
+seeded output gradients, from the chunk states of one untimed forward), with
+its own roofline and the oracle's backward timed on a slice of the channels.
 """
 from __future__ import annotations
 
@@ -43,6 +47,13 @@ HBM_PEAK_GBPS = 8000.0
 #                     + u = delta*x 2 + fma D*x 2 = 30
 FLOPEQ_PER_UPDATE = 16.0
 FLOPEQ_PER_ROW_STEP = 30.0
+# Backward, per state update: exp(delta*A) 8; delta*A, u*B, h fma (recompute);
+# g = C*dyp + mu, mu = Abar*g, sum g*B, da = g*h, da*Abar, sum da*Abar*A,
+# dA += .*delta, dB += g*u, dC += dyp*h: 12 ops, 2 each = 32.  Per (b, t, d):
+# softplus 26, sigmoid for its derivative (exp 8, rcp 8, add 2) 18, u = delta*x,
+# dDelta fma, the clip/softplus factor, dx fma, dD fma (2 each) 10 = 54.
+FLOPEQ_BWD_PER_UPDATE = 32.0
+FLOPEQ_BWD_PER_ROW_STEP = 54.0
 
 PROFILES = os.path.join(HERE, "profiles")
 KERNEL_SRC = os.path.join(HERE, "selective_state_space_scan_amd", "csrc", "ssm_scan.hip")
@@ -59,6 +70,19 @@ def algorithmic_bytes(w, e: int) -> int:
 def algorithmic_flops(w, valid_steps: int) -> float:
     """FMA-equivalent FLOPs of the method's arithmetic (see FLOPEQ_* above)."""
     return valid_steps * w.dim * (w.dstate * FLOPEQ_PER_UPDATE + FLOPEQ_PER_ROW_STEP)
+
+
+def algorithmic_bytes_bwd(w, e: int, chunk_len: int) -> int:
+    """Bytes the backward must move: x, delta, dy read and dx, ddelta written
+    ([B,L,D] each, io dtype); B, C read (io) and dB, dC written (fp32)
+    ([B,L,N] each); the chunk states read; A_log, D, dh_last read; dA_log, dD,
+    dh0 written."""
+    bld = w.batch * w.seqlen * w.dim
+    bln = w.batch * w.seqlen * w.dstate
+    n_chunks = (w.seqlen + chunk_len - 1) // chunk_len
+    bdn = w.batch * w.dim * w.dstate
+    return (5 * bld * e + 2 * bln * e + 2 * bln * 4 + (n_chunks - 1) * bdn * 4 + 2 * w.dim * w.dstate * 4
+            + 2 * w.dim * 4 + 2 * bdn * 4)
 
 
 def measured_traffic(w):
@@ -114,6 +138,8 @@ def main() -> int:
     ap.add_argument("--rotate", type=int, default=3, help="input copies rotated between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (default: min(16, cpus))")
+    ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
+                    help="measure the forward (default) or the backward")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="instead of the benchmark, run a plain device copy of this many MiB three times "
                          "(reference reading for the HBM byte counters)")
@@ -143,6 +169,8 @@ def main() -> int:
         return 0
     w = I.WORKLOADS[args.workload]
     inp = I.make_inputs(w, I.seed_for(args.workload))
+    if args.which == "bwd":
+        return bench_bwd(args, w, inp)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     dt = torch.bfloat16 if w.io == "bf16" else torch.float32
@@ -237,6 +265,117 @@ def main() -> int:
     if not args.no_cpu_baseline:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
         out["cpu_baseline"] = cpu_baseline(inp, w, threads)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+def cpu_baseline_bwd(inp, cot, w, threads: int, channels: int) -> dict:
+    """The fp64 oracle's backward on the first `channels` channels of the
+    workload (every batch row and step): a bounded sample."""
+    import oracle
+    oracle.build()
+    sl = (slice(None), slice(None), slice(0, channels))
+    t0 = time.perf_counter()
+    oracle.selective_scan_bwd(inp["x"][sl], inp["delta"][sl], inp["A_log"][:channels], inp["B"], inp["C"],
+                              inp["D"][:channels], cot["dy"][sl], valid_len=inp["valid_len"],
+                              dh_last=cot["dh_last"][:, :channels], delta_clamp=w.delta_clamp, nthreads=threads)
+    dt = time.perf_counter() - t0
+    steps = w.batch * w.seqlen if inp["valid_len"] is None else int(np.sum(inp["valid_len"]))
+    upd = steps * channels * w.dstate
+    used = min(threads, w.batch)  # the oracle's backward deals batch rows to threads
+    return {"value": upd / dt, "unit": "state-updates/s", "cores": used, "kind": "oracle",
+            "sample": f"channels 0..{channels - 1} of {w.name}, every row and step ({upd} state updates, "
+                      f"{dt:.2f} s wall, {used} threads over batch rows; fp64, gcc -O2)"}
+
+
+def bench_bwd(args, w, inp) -> int:
+    import torch
+
+    import selective_state_space_scan_amd as ssm
+    from selective_state_space_scan_amd import inputs as I
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    dt = torch.bfloat16 if w.io == "bf16" else torch.float32
+    cot = I.make_cotangents(w, I.seed_for(args.workload) + 500)
+    cl = ssm.bwd_chunk_len(w.dstate)
+    A_log = torch.from_numpy(inp["A_log"]).to(dev)
+    D = torch.from_numpy(inp["D"]).to(dev)
+    vl = None if inp["valid_len"] is None else torch.from_numpy(inp["valid_len"]).to(dev)
+    base = {k: torch.from_numpy(inp[k]).to(dev).to(dt).contiguous() for k in ("x", "delta", "B", "C")}
+    base["dy"] = torch.from_numpy(cot["dy"]).to(dev).to(dt)
+    dhl = torch.from_numpy(cot["dh_last"]).to(dev)
+    sets = []
+    for r in range(max(1, args.rotate)):
+        s = {k: (v if r == 0 else v.clone()) for k, v in base.items()}
+        # the forward (untimed) leaves the chunk states the backward recomputes from
+        _, _, s["cs"] = ssm.selective_scan_fwd(s["x"], s["delta"], A_log, s["B"], s["C"], D, vl,
+                                               delta_clamp=w.delta_clamp, return_chunk_states=True, chunk_len=cl)
+        sets.append(s)
+    dims = ssm.ssm_scan_dims()
+    dims.batch, dims.seqlen, dims.dim, dims.dstate = w.batch, w.seqlen, w.dim, w.dstate
+    dims.io_dtype = ssm.SSM_IO_BF16 if w.io == "bf16" else ssm.SSM_IO_F32
+    ws = torch.empty(ssm.bwd_workspace_bytes(dims), dtype=torch.uint8, device=dev)
+
+    def step(k: int):
+        s = sets[k % len(sets)]
+        ssm.selective_scan_bwd(s["x"], s["delta"], A_log, s["B"], s["C"], D, vl, s["dy"], s["cs"], dh_last=dhl,
+                               delta_clamp=w.delta_clamp, workspace=ws)
+
+    for k in range(args.warmup):
+        step(k)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        step(k)
+        ev[k][1].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    ms_per_step = t_start.elapsed_time(t_end) / args.steps
+    kern_avg_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    steps_valid = w.batch * w.seqlen if inp["valid_len"] is None else int(np.sum(inp["valid_len"]))
+    updates = steps_valid * w.dim * w.dstate
+    e = 2 if w.io == "bf16" else 4
+    nbytes = algorithmic_bytes_bwd(w, e, cl)
+    flops = steps_valid * w.dim * (w.dstate * FLOPEQ_BWD_PER_UPDATE + FLOPEQ_BWD_PER_ROW_STEP)
+    gbps = nbytes / (kern_avg_ms * 1e-3) / 1e9
+    tflops = flops / (kern_avg_ms * 1e-3) / 1e12
+    if flops / (FP32_VECTOR_PEAK_TFLOPS * 1e12) >= nbytes / (HBM_PEAK_GBPS * 1e9):
+        roof = {"bound": "alu", "achieved": round(tflops, 3), "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tflops / FP32_VECTOR_PEAK_TFLOPS, 4), "traffic": None}
+    else:
+        roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None}
+    roof.update({"kernel": "ssm_bwd_kernel + ssm_bwd_reduce_kernel", "kernel_avg_ms": round(kern_avg_ms, 5),
+                 "hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes": nbytes,
+                 "algorithmic_tflop": flops / 1e12, "traffic_unit": "bytes per launch"})
+    out = {
+        "metric": "selective-scan backward state-updates/s (B·L·D·N) + HBM GB/s",
+        "value": updates / (ms_per_step * 1e-3),
+        "unit": "state-updates/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "hbm_gbps": round(nbytes / (ms_per_step * 1e-3) / 1e9, 1),
+        "config": {"workload": w.name, "pass": "backward", "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim,
+                   "dstate": w.dstate, "io": w.io, "state_updates_per_step": updates, "chunk_len": cl,
+                   "input_copies_rotated": len(sets)},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        threads = args.cpu_threads or min(16, os.cpu_count() or 1)
+        out["cpu_baseline"] = cpu_baseline_bwd(inp, cot, w, threads, channels=min(w.dim, 128))
     print(json.dumps(out), flush=True)
     return 0
 

@@ -218,7 +218,7 @@ typedef struct ssm_scan_bwd_io {
   int64_t workspace_bytes;
 } ssm_scan_bwd_io;
 
-/* The backward's time tile for this dstate (64, 32 or 16 for dstate 16, 32 or
+/* The backward's time tile for this dstate (32, 16 or 8 for dstate 16, 32 or
  * 64; 0 if unsupported): the chunk_len the forward must save chunk_states at. */
 int64_t ssm_scan_bwd_chunk_len(int64_t dstate);
 

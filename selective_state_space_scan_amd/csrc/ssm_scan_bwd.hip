@@ -74,6 +74,7 @@ struct BwdParams {
   float* ws_dD;  // [nb, nd]
   float* ws_db;  // [nb, nd]
   int64_t L;
+  int64_t n_chunks;  // chunk states per row (chunks of the 4-wave tile)
   int32_t nb;
   int32_t nd;
   int32_t n_cg;
@@ -83,7 +84,11 @@ struct BwdParams {
 };
 
 constexpr int kBwdK = 2;  // steps per lane and sub-chunk
-constexpr int kBwdW = 8;  // waves per workgroup
+// Waves per workgroup: 4 when the grid fills the GPU (two workgroups share a
+// CU and cover each other's barriers), 8 for small grids (more waves per
+// (row, channel group)).  The chunk length of the saved states is the 4-wave
+// tile; an 8-wave tile reads every other chunk state.
+constexpr int kBwdW = 4;
 
 template <int G>
 constexpr int64_t bwd_tile_g = kBwdW * (4 / G) * kBwdK;
@@ -103,10 +108,10 @@ int64_t bwd_tile(int64_t N) {
 
 __device__ __forceinline__ float sigmoid_f32(float v) { return __builtin_amdgcn_rcpf(1.0f + fast_exp2(-v * kLog2e)); }
 
-template <typename IO, int G, bool SOFTPLUS, bool CLAMP, bool GATE>
-__global__ __launch_bounds__(64 * kBwdW, 2) void ssm_bwd_kernel(BwdParams p) {
+template <typename IO, int G, int W, bool SOFTPLUS, bool CLAMP, bool GATE>
+__global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
   constexpr int K = kBwdK;
-  constexpr int W = kBwdW;
+  constexpr int CS = W / kBwdW;  // saved chunks per tile
   constexpr int N = 16 * G;
   constexpr int QR = 4 / G;
   constexpr int SUB = W * QR;  // sub-chunks per tile
@@ -119,7 +124,7 @@ __global__ __launch_bounds__(64 * kBwdW, 2) void ssm_bwd_kernel(BwdParams p) {
   constexpr int PPL = (PAIRS + NT - 1) / NT;
   constexpr int E = Elem<IO>::kBytes;
   static_assert(SUB % 4 == 0, "sub-chunk records are read as quads");
-  static_assert(SUB * G == 32 && NT == 512, "one reducing thread per (16-lane row, state)");
+  static_assert(SUB * G * 16 == NT, "one reducing thread per (16-lane row, state)");
 
   // Sub-chunk records, float4 quads as in the forward: index
   // ((j * N/4 + n/4) * 16 + c) * 4 + n%4.  agg_b: forward b_total, then the
@@ -333,7 +338,8 @@ __global__ __launch_bounds__(64 * kBwdW, 2) void ssm_bwd_kernel(BwdParams p) {
         if (kt == 0)
           h = (p.h0 != nullptr) ? p.h0[state_block + pair_offset(k)] : 0.0f;
         else
-          h = p.chunk_states[((static_cast<int64_t>(b) * n_tiles + kt - 1) * nd + cg * 16) * N + pair_offset(k)];
+          h = p.chunk_states[((static_cast<int64_t>(b) * p.n_chunks + kt * CS - 1) * nd + cg * 16) * N +
+                             pair_offset(k)];
 #pragma unroll
         for (int jj = 0; jj < SUB; ++jj) {
           const float bb = pbw[jj * (N / 4) * 64];
@@ -385,8 +391,8 @@ __global__ __launch_bounds__(64 * kBwdW, 2) void ssm_bwd_kernel(BwdParams p) {
     for (int s = 0; s < 16; ++s) dAl[s] = 0.0f;
 
     // Staging for the sums over the 16 channels of a row: row block rb =
-    // j * G + g (32 of them) holds [s][c], so that the reducing thread of
-    // (rb, s) reads 16 consecutive floats.
+    // j * G + g (SUB * G = NT / 16 of them) holds [s][c], so that the
+    // reducing thread of (rb, s) reads 16 consecutive floats.
     const int rb = j * G + g;
     auto reduce_stage = [&](int i) {
       // thread (rb', s') sums the 16 channels of its row block for state s'
@@ -580,39 +586,43 @@ __global__ __launch_bounds__(256) void ssm_bwd_reduce_kernel(ReduceParams p) {
 }
 
 template <typename IO, int G, bool SP, bool CL, bool GATE>
-hipError_t bwd_launch_flags(const BwdParams& prm, hipStream_t stream) {
+hipError_t bwd_launch_flags(const BwdParams& prm, bool wide, hipStream_t stream) {
   const int64_t blocks = static_cast<int64_t>(prm.nb) * prm.n_cg;
-  hipLaunchKernelGGL((ssm_bwd_kernel<IO, G, SP, CL, GATE>), dim3(static_cast<unsigned>(blocks)), dim3(64 * kBwdW),
-                     0, stream, prm);
+  if (wide)
+    hipLaunchKernelGGL((ssm_bwd_kernel<IO, G, 2 * kBwdW, SP, CL, GATE>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(64 * 2 * kBwdW), 0, stream, prm);
+  else
+    hipLaunchKernelGGL((ssm_bwd_kernel<IO, G, kBwdW, SP, CL, GATE>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(64 * kBwdW), 0, stream, prm);
   return hipGetLastError();
 }
 
 template <typename IO, int G>
-hipError_t bwd_launch(const BwdParams& prm, bool sp, hipStream_t stream) {
+hipError_t bwd_launch(const BwdParams& prm, bool sp, bool wide, hipStream_t stream) {
   const bool gate = prm.z != nullptr;
   if (sp) {
     if (prm.clamp)
-      return gate ? bwd_launch_flags<IO, G, true, true, true>(prm, stream)
-                  : bwd_launch_flags<IO, G, true, true, false>(prm, stream);
-    return gate ? bwd_launch_flags<IO, G, true, false, true>(prm, stream)
-                : bwd_launch_flags<IO, G, true, false, false>(prm, stream);
+      return gate ? bwd_launch_flags<IO, G, true, true, true>(prm, wide, stream)
+                  : bwd_launch_flags<IO, G, true, true, false>(prm, wide, stream);
+    return gate ? bwd_launch_flags<IO, G, true, false, true>(prm, wide, stream)
+                : bwd_launch_flags<IO, G, true, false, false>(prm, wide, stream);
   }
   if (prm.clamp)
-    return gate ? bwd_launch_flags<IO, G, false, true, true>(prm, stream)
-                : bwd_launch_flags<IO, G, false, true, false>(prm, stream);
-  return gate ? bwd_launch_flags<IO, G, false, false, true>(prm, stream)
-              : bwd_launch_flags<IO, G, false, false, false>(prm, stream);
+    return gate ? bwd_launch_flags<IO, G, false, true, true>(prm, wide, stream)
+                : bwd_launch_flags<IO, G, false, true, false>(prm, wide, stream);
+  return gate ? bwd_launch_flags<IO, G, false, false, true>(prm, wide, stream)
+              : bwd_launch_flags<IO, G, false, false, false>(prm, wide, stream);
 }
 
 template <typename IO>
-hipError_t bwd_launch_io(int G, const BwdParams& prm, bool sp, hipStream_t stream) {
+hipError_t bwd_launch_io(int G, const BwdParams& prm, bool sp, bool wide, hipStream_t stream) {
   switch (G) {
     case 1:
-      return bwd_launch<IO, 1>(prm, sp, stream);
+      return bwd_launch<IO, 1>(prm, sp, wide, stream);
     case 2:
-      return bwd_launch<IO, 2>(prm, sp, stream);
+      return bwd_launch<IO, 2>(prm, sp, wide, stream);
     default:
-      return bwd_launch<IO, 4>(prm, sp, stream);
+      return bwd_launch<IO, 4>(prm, sp, wide, stream);
   }
 }
 
@@ -741,6 +751,7 @@ int ssm_selective_scan_bwd(ssm_scan_t handle, const void* x, const void* delta, 
   prm.ws_dD = prm.ws_dA + nb * nd * N;
   prm.ws_db = prm.ws_dD + nb * nd;
   prm.L = L;
+  prm.n_chunks = n_tiles;
   prm.nb = static_cast<int32_t>(nb);
   prm.nd = static_cast<int32_t>(nd);
   prm.n_cg = static_cast<int32_t>(n_cg);
@@ -769,8 +780,12 @@ int ssm_selective_scan_bwd(ssm_scan_t handle, const void* x, const void* delta, 
     }
     return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
   }
-  hipError_t err = dims->io_dtype == SSM_IO_BF16 ? bwd_launch_io<uint16_t>(G, prm, dims->delta_softplus != 0, s)
-                                                 : bwd_launch_io<float>(G, prm, dims->delta_softplus != 0, s);
+  // Eight-wave workgroups when the (row, channel group) grid leaves CUs idle
+  // with two four-wave workgroups per CU.
+  const bool wide = nb * n_cg < 2 * static_cast<int64_t>(handle->cu_count);
+  hipError_t err = dims->io_dtype == SSM_IO_BF16
+                       ? bwd_launch_io<uint16_t>(G, prm, dims->delta_softplus != 0, wide, s)
+                       : bwd_launch_io<float>(G, prm, dims->delta_softplus != 0, wide, s);
   if (err != hipSuccess) return SSM_ERR_HIP;
   ReduceParams rp;
   rp.ws_dB = prm.ws_dB;

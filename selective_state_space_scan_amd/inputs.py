@@ -109,3 +109,15 @@ def small_workload(base: Workload, batch=None, seqlen=None, dim=None) -> Workloa
     """The same recipe at another size (for parity cases the oracle finishes quickly)."""
     return dataclasses.replace(base, name=base.name + "-small", batch=batch or base.batch,
                                seqlen=seqlen or base.seqlen, dim=dim or base.dim)
+
+
+def make_cotangents(w: Workload, seed: int) -> dict:
+    """Seeded gradients of the outputs for the backward: dy [batch, L, dim]
+    ~ N(0, 1) (bf16-exact for bf16 I/O) and dh_last [batch, dim, dstate]
+    ~ N(0, 1) fp32, drawn in that order from their own generator."""
+    rng = np.random.default_rng(seed)
+    dy = rng.standard_normal((w.batch, w.seqlen, w.dim), dtype=np.float32)
+    dh_last = rng.standard_normal((w.batch, w.dim, w.dstate), dtype=np.float32)
+    if w.io == "bf16":
+        dy = round_to_bf16(dy)
+    return dict(dy=dy, dh_last=dh_last)

@@ -167,7 +167,7 @@ def test_bwd_checks():
     import ctypes
     BIO = ssm.ssm_scan_bwd_io
     E = ssm.ssm_scan_fwd_extras
-    assert ssm.bwd_chunk_len(16) == 64 and ssm.bwd_chunk_len(32) == 32 and ssm.bwd_chunk_len(64) == 16
+    assert ssm.bwd_chunk_len(16) == 32 and ssm.bwd_chunk_len(32) == 16 and ssm.bwd_chunk_len(64) == 8
     assert ssm.bwd_chunk_len(8) == 0
     d = _dims(batch=2, seqlen=100, dim=32, dstate=16)
     need = ssm.bwd_workspace_bytes(d)
@@ -190,8 +190,8 @@ def test_bwd_checks():
     assert call(io(), **bad_x) == ssm.SSM_ERR_UNSUPPORTED  # misaligned input
     assert call(io(workspace_bytes=need - 4), **bad_x) == ssm.SSM_ERR_INVALID_ARG  # workspace too small
     assert call(io(workspace=None), **bad_x) == ssm.SSM_ERR_INVALID_ARG
-    assert call(io(chunk_states=None), **bad_x) == ssm.SSM_ERR_INVALID_ARG  # 100 steps > one 64-step tile
-    assert call(io(chunk_states=None), dims=_dims(batch=2, seqlen=64, dim=32, dstate=16), **bad_x) == \
+    assert call(io(chunk_states=None), **bad_x) == ssm.SSM_ERR_INVALID_ARG  # 100 steps > one 32-step tile
+    assert call(io(chunk_states=None), dims=_dims(batch=2, seqlen=32, dim=32, dstate=16), **bad_x) == \
         ssm.SSM_ERR_UNSUPPORTED  # one tile needs no chunk states
     for k in ("dy", "dx", "ddelta", "dA_log", "dB", "dC"):
         assert call(io(**{k: None}), **bad_x) == ssm.SSM_ERR_INVALID_ARG, k

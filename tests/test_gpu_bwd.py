@@ -120,3 +120,10 @@ def test_bwd_after_time_split_forward():
     """The chunk states of a time-split forward serve the backward equally."""
     w, inp = _case("bf16", 64, 2048, 1, 32, seed=13)
     _compare(_gpu(inp, "bf16", time_parts=4), _oracle(inp), 2e-2, "split fwd")
+
+
+def test_bwd_grid_filling_shape():
+    """A grid of 512 (row, channel group) workgroups takes the four-wave
+    kernel (smaller grids take the eight-wave one)."""
+    w, inp = _case("bf16", 16, 200, 4, 2048, seed=17, varlen=[200, 77, 130, 5])
+    _compare(_gpu(inp, "bf16"), _oracle(inp), 2e-2, "grid 512")
