@@ -56,7 +56,16 @@ FLOPEQ_BWD_PER_UPDATE = 32.0
 FLOPEQ_BWD_PER_ROW_STEP = 54.0
 
 PROFILES = os.path.join(HERE, "profiles")
-KERNEL_SRC = os.path.join(HERE, "selective_state_space_scan_amd", "csrc", "ssm_scan.hip")
+# The forward kernel's sources: a traffic record applies only to the build it was taken on.
+KERNEL_SRCS = [os.path.join(HERE, "selective_state_space_scan_amd", "csrc", f) for f in ("ssm_scan.hip", "ssm_internal.h")]
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SRCS:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()
 
 
 def algorithmic_bytes(w, e: int) -> int:
@@ -90,7 +99,6 @@ def measured_traffic(w):
     each scaled by the copy-kernel calibration) as recorded in profiles/, or
     None when there is no record for this workload or the kernel source has
     changed since it was taken."""
-    import hashlib
     path = os.path.join(PROFILES, f"traffic_ssm_fwd_kernel_{w.name}.txt")
     if not os.path.exists(path):
         return None
@@ -99,8 +107,7 @@ def measured_traffic(w):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             rec[k.strip()] = v.strip()
-    src_hash = hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()
-    if rec.get("kernel_source_sha256") != src_hash:
+    if rec.get("kernel_source_sha256") != kernel_source_hash():
         return None
     try:
         return int(float(rec["hbm_bytes_per_launch"]))
