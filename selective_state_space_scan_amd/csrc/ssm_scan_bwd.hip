@@ -135,6 +135,8 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) float agg_m[AGG];
   __shared__ __attribute__((aligned(16))) float agg_sd[16 * SDS];
   __shared__ __attribute__((aligned(16))) float a2s[16 * NS];
+  // Staging of step 0's dB / dC contributions (step 1's go to agg_b / agg_m).
+  __shared__ __attribute__((aligned(16))) float stg[2][AGG];
   __shared__ float red[2][NT];  // end of kernel: dD and dbias per lane
 
   const int64_t total = static_cast<int64_t>(p.nb) * p.n_cg;
@@ -191,6 +193,9 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
     dA_acc[k] = 0.0f;
   }
   float dD_acc = 0.0f, db_acc = 0.0f;  // this lane's steps, channel d (counted once per (t, d))
+  float dAl[16];  // this lane's dA contributions for its 16 states, over all tiles
+#pragma unroll
+  for (int s = 0; s < 16; ++s) dAl[s] = 0.0f;
 
   const int64_t xd_step = static_cast<int64_t>(nd) * E;
   const int64_t bc_step = static_cast<int64_t>(N) * E;
@@ -386,39 +391,17 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
       const float u0 = u[0];
       Unroll<0, 16>::run([&]<int S>() { hm[S] = __builtin_fmaf(ab[0][S], hp[S], row_bcast<S>(b0) * u0); });
     }
-    float dAl[16];
-#pragma unroll
-    for (int s = 0; s < 16; ++s) dAl[s] = 0.0f;
 
     // Staging for the sums over the 16 channels of a row: row block rb =
-    // j * G + g (SUB * G = NT / 16 of them) holds [s][c], so that the
-    // reducing thread of (rb, s) reads 16 consecutive floats.
+    // j * G + g (SUB * G = NT / 16 of them) holds [c][s], 16 floats per lane
+    // written as quads; quad q of lane c sits at quad slot q ^ (rb % 4), so
+    // that the reducing threads of four row blocks (one wave) reading the same
+    // (c, s) hit four different banks.
     const int rb = j * G + g;
-    auto reduce_stage = [&](int i) {
-      // thread (rb', s') sums the 16 channels of its row block for state s'
-      const int rr = tid >> 4, ss = tid & 15;
-      const float* pbs = agg_b + rr * 256 + ss * 16;
-      const float* pcs = agg_m + rr * 256 + ss * 16;
-      float sb = 0.0f, sc = 0.0f;
-#pragma unroll
-      for (int k4 = 0; k4 < 16; k4 += 4) {
-        const float4 vb = *reinterpret_cast<const float4*>(pbs + k4);
-        const float4 vc = *reinterpret_cast<const float4*>(pcs + k4);
-        sb += (vb.x + vb.y) + (vb.z + vb.w);
-        sc += (vc.x + vc.y) + (vc.z + vc.w);
-      }
-      const int jr = rr / G, gr = rr % G;
-      const int64_t t = t_tile + jr * K + i;
-      if (t < len) {
-        wdB[t * N + 16 * gr + ss] = sb;
-        wdC[t * N + 16 * gr + ss] = sc;
-      }
-    };
-
 #pragma unroll
     for (int ii = 0; ii < K; ++ii) {
       const int i = K - 1 - ii;  // steps in reverse
-      // the state after step i and the one before it
+      // the state after step i (hn) and the one before it (hb)
       float hn[16];
       if (i == 1) {
         float b1 = bv[1];
@@ -429,27 +412,41 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
 #pragma unroll
         for (int s = 0; s < 16; ++s) hn[s] = hm[s];
       }
-      const float(&hb)[16] = (i == 1) ? hm : hp;  // state before step i
-      float ci = cv[i];
-      float bi = bv[i];
-      asm volatile("" : "+v"(ci), "+v"(bi));
+      const float(&hb)[16] = (i == 1) ? hm : hp;
       const float yi = dyp[i];
-      float sgb = 0.0f, sda = 0.0f, ypre = 0.0f;
-      float* pbs = agg_b + rb * 256 + c;
-      float* pcs = agg_m + rb * 256 + c;
-      Unroll<0, 16>::run([&]<int S>() {
-        const float gg = __builtin_fmaf(row_bcast<S>(ci), yi, mu[S]);  // adjoint of the state after step i
-        sgb = __builtin_fmaf(gg, row_bcast<S>(bi), sgb);
-        const float daa = gg * hb[S] * ab[i][S];
-        sda = __builtin_fmaf(daa, A2[S], sda);
-        dAl[S] = __builtin_fmaf(daa, dl[i], dAl[S]);
-        if constexpr (GATE) ypre = __builtin_fmaf(row_bcast<S>(ci), hn[S], ypre);
-        pbs[S * 16] = gg * u[i];
-        pcs[S * 16] = yi * hn[S];
-        mu[S] = ab[i][S] * gg;
-      });
-      sgb = sum_state_groups<G>(sgb);
-      sda = sum_state_groups<G>(sda);
+      // mu becomes the adjoint of the state after step i: mu + dyp * C
+      axpy16_row_bcast(mu, cv[i], yi);
+      float sg4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      dot16_row_bcast(sg4, bv[i], mu);  // sum_n g B
+      float ypre = 0.0f;
+      if constexpr (GATE) {
+        float yp4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        dot16_row_bcast(yp4, cv[i], hn);
+        ypre = (yp4[0] + yp4[1]) + (yp4[2] + yp4[3]);
+      }
+      float sda4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      float vb[16], vc[16];
+#pragma unroll
+      for (int s = 0; s < 16; ++s) {
+        const float daa = mu[s] * hb[s] * ab[i][s];
+        sda4[s & 3] = __builtin_fmaf(daa, A2[s], sda4[s & 3]);
+        dAl[s] = __builtin_fmaf(daa, dl[i], dAl[s]);
+        vb[s] = mu[s] * u[i];
+        vc[s] = yi * hn[s];
+        mu[s] = ab[i][s] * mu[s];
+      }
+      {
+        float* pbs = (i == 1 ? agg_b : stg[0]) + rb * 256 + c * 16;
+        float* pcs = (i == 1 ? agg_m : stg[1]) + rb * 256 + c * 16;
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int slot = (q4 ^ (rb & 3)) * 4;
+          *reinterpret_cast<float4*>(pbs + slot) = make_float4(vb[4 * q4], vb[4 * q4 + 1], vb[4 * q4 + 2], vb[4 * q4 + 3]);
+          *reinterpret_cast<float4*>(pcs + slot) = make_float4(vc[4 * q4], vc[4 * q4 + 1], vc[4 * q4 + 2], vc[4 * q4 + 3]);
+        }
+      }
+      const float sgb = sum_state_groups<G>((sg4[0] + sg4[1]) + (sg4[2] + sg4[3]));
+      const float sda = sum_state_groups<G>((sda4[0] + sda4[1]) + (sda4[2] + sda4[3]));
       if constexpr (GATE) ypre = sum_state_groups<G>(ypre) + dskip * xv[i];
       const float ddt = __builtin_fmaf(xv[i], sgb, sda * kLn2);  // A = A2 ln 2
       const float ddraw = ddt * fac[i];
@@ -470,32 +467,54 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
         Elem<IO>::store(rdd, off_xd, sx, 0.0f);
         if constexpr (GATE) Elem<IO>::store(rdz, off_xd, sx, 0.0f);
       }
-      __syncthreads();
-      reduce_stage(i);
-      __syncthreads();
     }
-
-    // dA: the lane's two steps, summed over the sub-chunks of the tile by the
-    // walk lanes (staged [state][channel][j] through agg_b: 16 N rows of SUB).
-#pragma unroll
-    for (int s = 0; s < 16; ++s) agg_b[((16 * g + s) * 16 + c) * SUB + j] = dAl[s];
     __syncthreads();
+    {
+      // thread (rr, ss) sums the 16 channels of row block rr for state ss, both steps
+      const int rr = tid >> 4, ss = tid & 15;
+      const int off = rr * 256 + (((ss >> 2) ^ (rr & 3)) * 4) + (ss & 3);
+      float sb1 = 0.0f, sc1 = 0.0f, sb0 = 0.0f, sc0 = 0.0f;
 #pragma unroll
-    for (int k = 0; k < PPL; ++k) {
-      if (pair_valid(k)) {
-        int cc, n;
-        pair_of(k, cc, n);
-        const float* pa = agg_b + (n * 16 + cc) * SUB;
-        float s4 = 0.0f;
-#pragma unroll
-        for (int u4 = 0; u4 < SUB; u4 += 4) {
-          const float4 v = *reinterpret_cast<const float4*>(pa + u4);
-          s4 += (v.x + v.y) + (v.z + v.w);
-        }
-        dA_acc[k] += s4;
+      for (int cc = 0; cc < 16; ++cc) {
+        sb1 += agg_b[off + cc * 16];
+        sc1 += agg_m[off + cc * 16];
+        sb0 += stg[0][off + cc * 16];
+        sc0 += stg[1][off + cc * 16];
+      }
+      const int jr = rr / G, gr = rr % G;
+      const int64_t t0 = t_tile + jr * K;
+      const int n = 16 * gr + ss;
+      if (t0 < len) {
+        wdB[t0 * N + n] = sb0;
+        wdC[t0 * N + n] = sc0;
+      }
+      if (t0 + 1 < len) {
+        wdB[(t0 + 1) * N + n] = sb1;
+        wdC[(t0 + 1) * N + n] = sc1;
       }
     }
-    __syncthreads();  // the next tile's pass 1 overwrites agg_b
+    __syncthreads();  // the next tile's pass 1 overwrites agg_b / agg_m
+  }
+
+  // dA: each lane's 16 states summed over the lanes of its channel (the
+  // sub-chunks j), staged [state][channel][j] through agg_b.
+#pragma unroll
+  for (int s = 0; s < 16; ++s) agg_b[((16 * g + s) * 16 + c) * SUB + j] = dAl[s];
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < PPL; ++k) {
+    if (pair_valid(k)) {
+      int cc, n;
+      pair_of(k, cc, n);
+      const float* pa = agg_b + (n * 16 + cc) * SUB;
+      float s4 = 0.0f;
+#pragma unroll
+      for (int u4 = 0; u4 < SUB; u4 += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(pa + u4);
+        s4 += (v.x + v.y) + (v.z + v.w);
+      }
+      dA_acc[k] = s4;
+    }
   }
 
   // ---- per-(b, d) and per-(b, d, n) results ----
