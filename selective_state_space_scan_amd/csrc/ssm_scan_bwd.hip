@@ -70,9 +70,18 @@ struct BwdParams {
   float* dh0;
   float* ws_dB;  // [n_cg, nb, L, N] partial sums over the 16 channels of a group
   float* ws_dC;
-  float* ws_dA;  // [nb, nd, N]
-  float* ws_dD;  // [nb, nd]
-  float* ws_db;  // [nb, nd]
+  float* ws_dA;  // [n_parts, nb, nd, N]
+  float* ws_dD;  // [n_parts, nb, nd]
+  float* ws_db;  // [n_parts, nb, nd]
+  // Time split (small batches): parts of part_len steps (whole tiles).  The
+  // fold kernel leaves, for parts 1 .. n_parts-1, the adjoint folded from zero
+  // over the part (ws_M [n_parts-1, nb, nd, N]) and its delta sums (ws_S
+  // [n_parts-1, nb, nd]); part p then starts from dh_last carried back through
+  // parts n_parts-1 .. p+1.
+  float* ws_M;
+  float* ws_S;
+  int64_t part_len;
+  int32_t n_parts;
   int64_t L;
   int64_t n_chunks;  // chunk states per row (chunks of the 4-wave tile)
   int32_t nb;
@@ -108,7 +117,9 @@ int64_t bwd_tile(int64_t N) {
 
 __device__ __forceinline__ float sigmoid_f32(float v) { return __builtin_amdgcn_rcpf(1.0f + fast_exp2(-v * kLog2e)); }
 
-template <typename IO, int G, int W, bool SOFTPLUS, bool CLAMP, bool GATE>
+// FOLD: the fold kernel of the time split (pass 1 and the reverse walk only,
+// over parts 1 .. n_parts-1).  Otherwise the backward over every part.
+template <typename IO, int G, int W, bool SOFTPLUS, bool CLAMP, bool GATE, bool FOLD>
 __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
   constexpr int K = kBwdK;
   constexpr int CS = W / kBwdW;  // saved chunks per tile
@@ -139,11 +150,13 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) float stg[2][AGG];
   __shared__ float red[2][NT];  // end of kernel: dD and dbias per lane
 
-  const int64_t total = static_cast<int64_t>(p.nb) * p.n_cg;
+  const int64_t groups = static_cast<int64_t>(p.nb) * p.n_cg;
+  const int64_t total = groups * (FOLD ? p.n_parts - 1 : p.n_parts);
   const int64_t bid = blockIdx.x;
   const int64_t per_xcd = total / 8;
   const int64_t logical = (bid < per_xcd * 8) ? (bid % 8) * per_xcd + bid / 8 : bid;
-  const int b = static_cast<int>(logical / p.n_cg);
+  const int part = static_cast<int>(logical / groups) + (FOLD ? 1 : 0);
+  const int b = static_cast<int>((logical % groups) / p.n_cg);
   const int cg = static_cast<int>(logical % p.n_cg);
 
   const int tid = threadIdx.x;
@@ -156,12 +169,17 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
   const int j = w * QR + q;
   const int d = cg * 16 + c;
   const int nd = p.nd;
-  const int64_t L = p.L;
-  int64_t len = L;
+  // This workgroup's steps [t_begin, t_begin + L); below, step indices are
+  // relative to t_begin.
+  const int64_t t_begin = part * p.part_len;
+  const int64_t L = (p.L - t_begin < p.part_len) ? p.L - t_begin : p.part_len;
+  int64_t len = p.L;
   if (p.valid_len != nullptr) {
     const int64_t v = p.valid_len[b];
-    len = v < 0 ? 0 : (v > L ? L : v);
+    len = v < 0 ? 0 : (v > p.L ? p.L : v);
   }
+  len -= t_begin;
+  len = len < 0 ? 0 : (len > L ? L : len);
 
   for (int k = tid; k < 16 * N; k += NT) {
     const int cc = k / N, n = k % N;
@@ -183,14 +201,31 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
   };
   const int64_t state_block = (static_cast<int64_t>(b) * nd + cg * 16) * N;
   const int64_t n_tiles = (L + T - 1) / T;
+  const int64_t tile0 = t_begin / T;  // global index of the part's first tile
+  const int64_t sblock = static_cast<int64_t>(p.nb) * nd * N;
 
   // The adjoint carry (mu entering the current tile from the future) and the
-  // per-pair dA accumulator, held by the walk lanes.
-  float mu_carry[PPL], dA_acc[PPL];
+  // per-pair dA accumulator, held by the walk lanes.  A part other than the
+  // last starts from dh_last carried back through the later parts' folds.
+  float mu_carry[PPL], dA_acc[PPL], part_sd[PPL];
 #pragma unroll
   for (int k = 0; k < PPL; ++k) {
-    mu_carry[k] = (p.dh_last != nullptr && pair_valid(k)) ? p.dh_last[state_block + pair_offset(k)] : 0.0f;
     dA_acc[k] = 0.0f;
+    part_sd[k] = 0.0f;
+    mu_carry[k] = 0.0f;
+    if (!FOLD && pair_valid(k)) {
+      float mu = (p.dh_last != nullptr) ? p.dh_last[state_block + pair_offset(k)] : 0.0f;
+      if (part < p.n_parts - 1) {
+        int cc, n;
+        pair_of(k, cc, n);
+        const float a2 = -expf(p.A_log[static_cast<int64_t>(cg * 16 + cc) * N + n]) * kLog2e;
+        for (int qp = p.n_parts - 1; qp > part; --qp) {
+          const float sdq = p.ws_S[(static_cast<int64_t>(qp - 1) * p.nb + b) * nd + cg * 16 + cc];
+          mu = __builtin_fmaf(fast_exp2(a2 * sdq), mu, p.ws_M[(qp - 1) * sblock + state_block + pair_offset(k)]);
+        }
+      }
+      mu_carry[k] = mu;
+    }
   }
   float dD_acc = 0.0f, db_acc = 0.0f;  // this lane's steps, channel d (counted once per (t, d))
   float dAl[16];  // this lane's dA contributions for its 16 states, over all tiles
@@ -199,21 +234,23 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
 
   const int64_t xd_step = static_cast<int64_t>(nd) * E;
   const int64_t bc_step = static_cast<int64_t>(N) * E;
+  const int64_t xd_base = (b * p.L + t_begin) * xd_step, bc_base = (b * p.L + t_begin) * bc_step;
   const int64_t xd_row = L * xd_step, bc_row = L * bc_step;
-  const rsrc_t rx = make_rsrc(static_cast<const char*>(p.x) + b * xd_row, xd_row);
-  const rsrc_t rd = make_rsrc(static_cast<const char*>(p.delta) + b * xd_row, xd_row);
-  const rsrc_t rdy = make_rsrc(static_cast<const char*>(p.dy) + b * xd_row, xd_row);
-  const rsrc_t rz = make_rsrc(GATE ? static_cast<const char*>(p.z) + b * xd_row : nullptr, GATE ? xd_row : 0);
-  const rsrc_t rdx = make_rsrc(static_cast<char*>(p.dx) + b * xd_row, xd_row);
-  const rsrc_t rdd = make_rsrc(static_cast<char*>(p.ddelta) + b * xd_row, xd_row);
-  const rsrc_t rdz = make_rsrc(GATE ? static_cast<char*>(p.dz) + b * xd_row : nullptr, GATE ? xd_row : 0);
-  const rsrc_t rb = make_rsrc(static_cast<const char*>(p.B) + b * bc_row, bc_row);
-  const rsrc_t rc = make_rsrc(static_cast<const char*>(p.C) + b * bc_row, bc_row);
+  const rsrc_t rx = make_rsrc(static_cast<const char*>(p.x) + xd_base, xd_row);
+  const rsrc_t rd = make_rsrc(static_cast<const char*>(p.delta) + xd_base, xd_row);
+  const rsrc_t rdy = make_rsrc(static_cast<const char*>(p.dy) + xd_base, xd_row);
+  const rsrc_t rz = make_rsrc(GATE ? static_cast<const char*>(p.z) + xd_base : nullptr, GATE ? xd_row : 0);
+  const rsrc_t rdx = make_rsrc(FOLD ? nullptr : static_cast<char*>(p.dx) + xd_base, FOLD ? 0 : xd_row);
+  const rsrc_t rdd = make_rsrc(FOLD ? nullptr : static_cast<char*>(p.ddelta) + xd_base, FOLD ? 0 : xd_row);
+  const rsrc_t rdz =
+      make_rsrc(GATE && !FOLD ? static_cast<char*>(p.dz) + xd_base : nullptr, GATE && !FOLD ? xd_row : 0);
+  const rsrc_t rb = make_rsrc(static_cast<const char*>(p.B) + bc_base, bc_row);
+  const rsrc_t rc = make_rsrc(static_cast<const char*>(p.C) + bc_base, bc_row);
   const uint32_t off_xd = static_cast<uint32_t>((j * K * nd + d) * E);
   const uint32_t off_bc = static_cast<uint32_t>((j * K * N + 16 * g + c) * E);
-  // dB / dC partials of this channel group: [n_cg, nb, L, N]
-  float* const wdB = p.ws_dB + ((static_cast<int64_t>(cg) * p.nb + b) * L) * N;
-  float* const wdC = p.ws_dC + ((static_cast<int64_t>(cg) * p.nb + b) * L) * N;
+  // dB / dC partials of this channel group: [n_cg, nb, L, N], from the part's first step
+  float* const wdB = p.ws_dB + ((static_cast<int64_t>(cg) * p.nb + b) * p.L + t_begin) * N;
+  float* const wdC = p.ws_dC + ((static_cast<int64_t>(cg) * p.nb + b) * p.L + t_begin) * N;
 
   __syncthreads();  // a2s is written
 
@@ -222,6 +259,7 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
     const int64_t left = len - t_tile - j * K;  // valid steps from this lane's first step
     if (len <= t_tile) {
       // A tile wholly in the padding: zero gradients, the adjoint passes through.
+      if constexpr (FOLD) continue;
 #pragma unroll
       for (int i = 0; i < K; ++i) {
         if (j * K + i < L - t_tile && (G == 1 || (i % G) == g)) {
@@ -241,11 +279,12 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
       const bool ok = i < left;
       const uint32_t sx = static_cast<uint32_t>((t_tile + i) * xd_step);
       const uint32_t sb = static_cast<uint32_t>((t_tile + i) * bc_step);
-      xv[i] = ok ? Elem<IO>::template load<kStream>(rx, off_xd, sx) : 0.0f;
+      // the fold needs neither x nor B (only the adjoint input dyp * C)
+      xv[i] = (ok && !FOLD) ? Elem<IO>::template load<kStream>(rx, off_xd, sx) : 0.0f;
       dlr[i] = ok ? Elem<IO>::template load<kStream>(rd, off_xd, sx) : 0.0f;
       dyv[i] = ok ? Elem<IO>::template load<kStream>(rdy, off_xd, sx) : 0.0f;
       zv[i] = (GATE && ok) ? Elem<IO>::template load<kStream>(rz, off_xd, sx) : 0.0f;
-      bv[i] = ok ? Elem<IO>::template load<0>(rb, off_bc, sb) : 0.0f;
+      bv[i] = (ok && !FOLD) ? Elem<IO>::template load<0>(rb, off_bc, sb) : 0.0f;
       cv[i] = ok ? Elem<IO>::template load<0>(rc, off_bc, sb) : 0.0f;
     }
     float A2[16];
@@ -297,7 +336,8 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
       const float ui = u[i];
       Unroll<0, 16>::run([&]<int S>() {
         ab[i][S] = fast_exp2(dl[i] * A2[S]);
-        bt[S] = (i == 0) ? row_bcast<S>(bi) * ui : __builtin_fmaf(ab[i][S], bt[S], row_bcast<S>(bi) * ui);
+        if constexpr (!FOLD)
+          bt[S] = (i == 0) ? row_bcast<S>(bi) * ui : __builtin_fmaf(ab[i][S], bt[S], row_bcast<S>(bi) * ui);
       });
     }
     {
@@ -313,7 +353,8 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
       float* pm = agg_m + ((j * (N / 4) + 4 * g) * 16 + c) * 4;
 #pragma unroll
       for (int s = 0; s < 16; s += 4) {
-        *reinterpret_cast<float4*>(pb + s * 16) = make_float4(bt[s], bt[s + 1], bt[s + 2], bt[s + 3]);
+        if constexpr (!FOLD)
+          *reinterpret_cast<float4*>(pb + s * 16) = make_float4(bt[s], bt[s + 1], bt[s + 2], bt[s + 3]);
         *reinterpret_cast<float4*>(pm + s * 16) = make_float4(mm[s], mm[s + 1], mm[s + 2], mm[s + 3]);
       }
       if (g == 0) agg_sd[c * SDS + j] = sd;
@@ -339,29 +380,40 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
           av[u4 + 2] = fast_exp2(a2 * v.z);
           av[u4 + 3] = fast_exp2(a2 * v.w);
         }
-        float h;
-        if (kt == 0)
-          h = (p.h0 != nullptr) ? p.h0[state_block + pair_offset(k)] : 0.0f;
-        else
-          h = p.chunk_states[((static_cast<int64_t>(b) * p.n_chunks + kt * CS - 1) * nd + cg * 16) * N +
-                             pair_offset(k)];
+        if constexpr (FOLD) {
 #pragma unroll
-        for (int jj = 0; jj < SUB; ++jj) {
-          const float bb = pbw[jj * (N / 4) * 64];
-          pbw[jj * (N / 4) * 64] = h;
-          h = __builtin_fmaf(av[jj], h, bb);
+          for (int u4 = 0; u4 < SUB; u4 += 4) {
+            const float4 v = *reinterpret_cast<const float4*>(psd + u4);
+            part_sd[k] += (v.x + v.y) + (v.z + v.w);
+          }
+        } else {
+          // the state entering the tile: h0, or the chunk state the forward saved
+          const int64_t gt = tile0 + kt;
+          float h;
+          if (gt == 0)
+            h = (p.h0 != nullptr) ? p.h0[state_block + pair_offset(k)] : 0.0f;
+          else
+            h = p.chunk_states[((static_cast<int64_t>(b) * p.n_chunks + gt * CS - 1) * nd + cg * 16) * N +
+                               pair_offset(k)];
+#pragma unroll
+          for (int jj = 0; jj < SUB; ++jj) {
+            const float bb = pbw[jj * (N / 4) * 64];
+            pbw[jj * (N / 4) * 64] = h;
+            h = __builtin_fmaf(av[jj], h, bb);
+          }
         }
         float mu = mu_carry[k];
 #pragma unroll
         for (int jj = SUB - 1; jj >= 0; --jj) {
           const float m = pmw[jj * (N / 4) * 64];
-          pmw[jj * (N / 4) * 64] = mu;
+          if constexpr (!FOLD) pmw[jj * (N / 4) * 64] = mu;
           mu = __builtin_fmaf(av[jj], mu, m);
         }
         mu_carry[k] = mu;
       }
     }
     __syncthreads();
+    if constexpr (FOLD) continue;  // the barrier above also orders the walk before the next pass 1
 
     // ---- pass 2: rebuild h over the lane's steps, run the adjoint back ----
     float hp[16], mu[16];
@@ -496,6 +548,20 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
     __syncthreads();  // the next tile's pass 1 overwrites agg_b / agg_m
   }
 
+  if constexpr (FOLD) {
+    // the part's adjoint fold from zero, and its delta sums per channel
+#pragma unroll
+    for (int k = 0; k < PPL; ++k) {
+      if (pair_valid(k)) {
+        int cc, n;
+        pair_of(k, cc, n);
+        p.ws_M[(part - 1) * sblock + state_block + pair_offset(k)] = mu_carry[k];
+        if (n == 0) p.ws_S[(static_cast<int64_t>(part - 1) * p.nb + b) * nd + cg * 16 + cc] = part_sd[k];
+      }
+    }
+    return;
+  }
+
   // dA: each lane's 16 states summed over the lanes of its channel (the
   // sub-chunks j), staged [state][channel][j] through agg_b.
 #pragma unroll
@@ -524,8 +590,8 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
       int cc, n;
       pair_of(k, cc, n);
       const int64_t o = state_block + pair_offset(k);
-      if (p.dh0 != nullptr) p.dh0[o] = mu_carry[k];
-      p.ws_dA[o] = dA_acc[k];
+      if (p.dh0 != nullptr && part == 0) p.dh0[o] = mu_carry[k];
+      p.ws_dA[part * sblock + o] = dA_acc[k];
     }
   }
   red[0][tid] = dD_acc;
@@ -539,14 +605,14 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
         s0 += red[0][ww * 64 + rr * 16 + tid];
         s1 += red[1][ww * 64 + rr * 16 + tid];
       }
-    p.ws_dD[static_cast<int64_t>(b) * nd + cg * 16 + tid] = s0;
-    p.ws_db[static_cast<int64_t>(b) * nd + cg * 16 + tid] = s1;
+    p.ws_dD[(static_cast<int64_t>(part) * p.nb + b) * nd + cg * 16 + tid] = s0;
+    p.ws_db[(static_cast<int64_t>(part) * p.nb + b) * nd + cg * 16 + tid] = s1;
   }
 }
 
 // Sums the partials in a fixed order: dB, dC over channel groups (zero past
-// each row's valid length), dA_log = A * sum over rows of dA, dD and dbias
-// over rows.
+// each row's valid length), dA_log = A * sum over (part, row) of dA, dD and
+// dbias over (part, row).
 struct ReduceParams {
   const float* ws_dB;
   const float* ws_dC;
@@ -562,6 +628,7 @@ struct ReduceParams {
   float* dbias;
   int64_t L;
   int32_t nb, nd, N, n_cg;
+  int32_t rows;  // n_parts * nb partial rows of dA, dD, dbias
 };
 
 __global__ __launch_bounds__(256) void ssm_bwd_reduce_kernel(ReduceParams p) {
@@ -589,12 +656,12 @@ __global__ __launch_bounds__(256) void ssm_bwd_reduce_kernel(ReduceParams p) {
     } else if (i < n_bc + n_dn) {
       const int64_t k = i - n_bc;
       float s = 0.0f;
-      for (int b = 0; b < p.nb; ++b) s += p.ws_dA[b * n_dn + k];
+      for (int b = 0; b < p.rows; ++b) s += p.ws_dA[b * n_dn + k];
       p.dA_log[k] = s * -expf(p.A_log[k]);
     } else {
       const int64_t dd = i - n_bc - n_dn;
       float s0 = 0.0f, s1 = 0.0f;
-      for (int b = 0; b < p.nb; ++b) {
+      for (int b = 0; b < p.rows; ++b) {
         s0 += p.ws_dD[b * p.nd + dd];
         s1 += p.ws_db[b * p.nd + dd];
       }
@@ -606,13 +673,22 @@ __global__ __launch_bounds__(256) void ssm_bwd_reduce_kernel(ReduceParams p) {
 
 template <typename IO, int G, bool SP, bool CL, bool GATE>
 hipError_t bwd_launch_flags(const BwdParams& prm, bool wide, hipStream_t stream) {
-  const int64_t blocks = static_cast<int64_t>(prm.nb) * prm.n_cg;
-  if (wide)
-    hipLaunchKernelGGL((ssm_bwd_kernel<IO, G, 2 * kBwdW, SP, CL, GATE>), dim3(static_cast<unsigned>(blocks)),
+  const int64_t groups = static_cast<int64_t>(prm.nb) * prm.n_cg;
+  if (prm.n_parts > 1) {
+    // the fold of parts 1 .. n_parts-1 first, on the same stream
+    hipLaunchKernelGGL((ssm_bwd_kernel<IO, G, kBwdW, SP, CL, GATE, true>),
+                       dim3(static_cast<unsigned>(groups * (prm.n_parts - 1))), dim3(64 * kBwdW), 0, stream, prm);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((ssm_bwd_kernel<IO, G, kBwdW, SP, CL, GATE, false>),
+                       dim3(static_cast<unsigned>(groups * prm.n_parts)), dim3(64 * kBwdW), 0, stream, prm);
+  } else if (wide) {
+    hipLaunchKernelGGL((ssm_bwd_kernel<IO, G, 2 * kBwdW, SP, CL, GATE, false>), dim3(static_cast<unsigned>(groups)),
                        dim3(64 * 2 * kBwdW), 0, stream, prm);
-  else
-    hipLaunchKernelGGL((ssm_bwd_kernel<IO, G, kBwdW, SP, CL, GATE>), dim3(static_cast<unsigned>(blocks)),
+  } else {
+    hipLaunchKernelGGL((ssm_bwd_kernel<IO, G, kBwdW, SP, CL, GATE, false>), dim3(static_cast<unsigned>(groups)),
                        dim3(64 * kBwdW), 0, stream, prm);
+  }
   return hipGetLastError();
 }
 
@@ -645,10 +721,14 @@ hipError_t bwd_launch_io(int G, const BwdParams& prm, bool sp, bool wide, hipStr
   }
 }
 
-// Workspace floats: dB and dC partials per channel group, dA per row, dD and
-// dbias per row.
+constexpr int64_t kBwdMaxParts = 8;
+
+// Workspace floats: dB and dC partials per channel group; dA, dD and dbias per
+// (part, row); the fold's adjoint and delta sums per (part >= 1, row) -- sized
+// for the largest split.
 int64_t bwd_ws_floats(int64_t nb, int64_t L, int64_t nd, int64_t N) {
-  return 2 * (nd / 16) * nb * L * N + nb * nd * N + 2 * nb * nd;
+  return 2 * (nd / 16) * nb * L * N + kBwdMaxParts * (nb * nd * N + 2 * nb * nd) +
+         (kBwdMaxParts - 1) * (nb * nd * N + nb * nd);
 }
 
 __global__ void zero_fill_kernel(float* dst, int64_t n) {
@@ -764,11 +844,31 @@ int ssm_selective_scan_bwd(ssm_scan_t handle, const void* x, const void* delta, 
   prm.ddelta = io->ddelta;
   prm.dz = ex.z != nullptr ? io->dz : nullptr;
   prm.dh0 = io->dh0;
+  // Time split: when the (row, channel group) grid leaves CUs idle, cut time
+  // into parts of whole tiles (at most 8, at least four tiles per part), as
+  // the forward does.
+  const int64_t groups = nb * n_cg;
+  const int64_t slots = 2 * static_cast<int64_t>(handle->cu_count);
+  int64_t parts = 1, part_len = L;
+  if (groups < slots) {
+    int64_t want = (2 * slots + groups - 1) / groups;
+    if (want > kBwdMaxParts) want = kBwdMaxParts;
+    if (want > n_tiles / 4) want = n_tiles / 4;
+    if (want > 1) {
+      const int64_t per = (n_tiles + want - 1) / want;
+      parts = (n_tiles + per - 1) / per;
+      part_len = per * T;
+    }
+  }
   prm.ws_dB = ws;
   prm.ws_dC = ws + n_cg * nb * L * N;
   prm.ws_dA = ws + 2 * n_cg * nb * L * N;
-  prm.ws_dD = prm.ws_dA + nb * nd * N;
-  prm.ws_db = prm.ws_dD + nb * nd;
+  prm.ws_dD = prm.ws_dA + kBwdMaxParts * nb * nd * N;
+  prm.ws_db = prm.ws_dD + kBwdMaxParts * nb * nd;
+  prm.ws_M = prm.ws_db + kBwdMaxParts * nb * nd;
+  prm.ws_S = prm.ws_M + (kBwdMaxParts - 1) * nb * nd * N;
+  prm.part_len = part_len;
+  prm.n_parts = static_cast<int32_t>(parts);
   prm.L = L;
   prm.n_chunks = n_tiles;
   prm.nb = static_cast<int32_t>(nb);
@@ -801,7 +901,7 @@ int ssm_selective_scan_bwd(ssm_scan_t handle, const void* x, const void* delta, 
   }
   // Eight-wave workgroups when the (row, channel group) grid leaves CUs idle
   // with two four-wave workgroups per CU.
-  const bool wide = nb * n_cg < 2 * static_cast<int64_t>(handle->cu_count);
+  const bool wide = parts == 1 && groups < slots;
   hipError_t err = dims->io_dtype == SSM_IO_BF16
                        ? bwd_launch_io<uint16_t>(G, prm, dims->delta_softplus != 0, wide, s)
                        : bwd_launch_io<float>(G, prm, dims->delta_softplus != 0, wide, s);
@@ -824,6 +924,7 @@ int ssm_selective_scan_bwd(ssm_scan_t handle, const void* x, const void* delta, 
   rp.nd = static_cast<int32_t>(nd);
   rp.N = static_cast<int32_t>(N);
   rp.n_cg = static_cast<int32_t>(n_cg);
+  rp.rows = static_cast<int32_t>(parts * nb);
   const int64_t work = nb * L * N + nd * N + nd;
   int64_t blocks = (work + 255) / 256;
   if (blocks > 4096) blocks = 4096;
