@@ -139,8 +139,10 @@ def cpu_baseline(inp, w, threads: int, min_seconds: float = 1.0) -> dict:
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    # The GPU settles to its sustained clock over the first ~100 launches
+    # (measured: 205 us average after 5 warm-up launches, 192 us after 200).
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", type=int, default=2, help="workload index (default: the headline one)")
     ap.add_argument("--rotate", type=int, default=3, help="input copies rotated between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
