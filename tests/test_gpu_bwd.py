@@ -127,3 +127,27 @@ def test_bwd_grid_filling_shape():
     kernel (smaller grids take the eight-wave one)."""
     w, inp = _case("bf16", 16, 200, 4, 2048, seed=17, varlen=[200, 77, 130, 5])
     _compare(_gpu(inp, "bf16"), _oracle(inp), 2e-2, "grid 512")
+
+
+def test_bwd_headline_shape():
+    """B8 L4096 D1024 N16 bf16 (the headline shape), every gradient against the
+    oracle's backward over the whole problem."""
+    import oracle
+    import torch
+    import selective_state_space_scan_amd as ssm
+    w = I.WORKLOADS[2]
+    inp = I.make_inputs(w, I.seed_for(2))
+    cot = I.make_cotangents(w, I.seed_for(2) + 500)
+    dev = to_device(inp, "bf16")
+    y, h, cs = ssm.selective_scan_fwd(dev["x"], dev["delta"], dev["A_log"], dev["B"], dev["C"], dev["D"], None,
+                                      return_chunk_states=True, chunk_len=ssm.bwd_chunk_len(w.dstate))
+    dy = torch.from_numpy(cot["dy"]).cuda().to(torch.bfloat16)
+    g = ssm.selective_scan_bwd(dev["x"], dev["delta"], dev["A_log"], dev["B"], dev["C"], dev["D"], None, dy, cs,
+                               dh_last=torch.from_numpy(cot["dh_last"]).cuda())
+    torch.cuda.synchronize()
+    g = {k: (None if v is None else v.float().cpu().numpy().astype(np.float64)) for k, v in g.items()}
+    r = oracle.selective_scan_bwd(inp["x"], inp["delta"], inp["A_log"], inp["B"], inp["C"], inp["D"], cot["dy"],
+                                  dh_last=cot["dh_last"], nthreads=8)
+    worst = {k: rel_err(g[k], r[k]) for k in GRADS if r.get(k) is not None and g.get(k) is not None}
+    print("headline", " ".join(f"{k} {v:.1e}" for k, v in worst.items()), flush=True)
+    assert all(v <= 2e-2 for v in worst.values()), worst
