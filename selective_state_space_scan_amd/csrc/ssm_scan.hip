@@ -256,8 +256,8 @@ __global__ __launch_bounds__(64 * W, kMinWavesPerSimd) void ssm_fwd_kernel(FwdPa
     for (int i = 0; i < K; ++i) {
       const bool ok = FULL || i < left;
       const uint32_t sx = static_cast<uint32_t>((t_tile + i) * xd_step);
-      xv[i] = ok ? Elem<IO>::template load<kStream>(rx, off_xd, sx) : 0.0f;
-      dv[i] = ok ? Elem<IO>::template load<kStream>(rd, off_xd, sx) : 0.0f;
+      xv[i] = ok ? Elem<IO>::template load<kCached>(rx, off_xd, sx) : 0.0f;
+      dv[i] = ok ? Elem<IO>::template load<kCached>(rd, off_xd, sx) : 0.0f;
     }
   };
 
@@ -415,7 +415,7 @@ __global__ __launch_bounds__(64 * W, kMinWavesPerSimd) void ssm_fwd_kernel(FwdPa
       if constexpr (GATE) {
         // y * silu(z), silu(z) = z / (1 + 2^(-z log2 e)); padded steps never load z
         const uint32_t sz = static_cast<uint32_t>((t_tile + i) * xd_step);
-        const float zv = (FULL || i < left) ? Elem<IO>::template load<kStream>(rz, off_xd, sz) : 0.0f;
+        const float zv = (FULL || i < left) ? Elem<IO>::template load<kCached>(rz, off_xd, sz) : 0.0f;
         yv0 *= zv * __builtin_amdgcn_rcpf(1.0f + fast_exp2(-zv * kLog2e));
       }
       const uint32_t sx = static_cast<uint32_t>((t_tile + i) * xd_step);

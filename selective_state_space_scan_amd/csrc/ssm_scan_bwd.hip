@@ -280,10 +280,10 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
       const uint32_t sx = static_cast<uint32_t>((t_tile + i) * xd_step);
       const uint32_t sb = static_cast<uint32_t>((t_tile + i) * bc_step);
       // the fold needs neither x nor B (only the adjoint input dyp * C)
-      xv[i] = (ok && !FOLD) ? Elem<IO>::template load<kStream>(rx, off_xd, sx) : 0.0f;
-      dlr[i] = ok ? Elem<IO>::template load<kStream>(rd, off_xd, sx) : 0.0f;
-      dyv[i] = ok ? Elem<IO>::template load<kStream>(rdy, off_xd, sx) : 0.0f;
-      zv[i] = (GATE && ok) ? Elem<IO>::template load<kStream>(rz, off_xd, sx) : 0.0f;
+      xv[i] = (ok && !FOLD) ? Elem<IO>::template load<kCached>(rx, off_xd, sx) : 0.0f;
+      dlr[i] = ok ? Elem<IO>::template load<kCached>(rd, off_xd, sx) : 0.0f;
+      dyv[i] = ok ? Elem<IO>::template load<kCached>(rdy, off_xd, sx) : 0.0f;
+      zv[i] = (GATE && ok) ? Elem<IO>::template load<kCached>(rz, off_xd, sx) : 0.0f;
       bv[i] = (ok && !FOLD) ? Elem<IO>::template load<0>(rb, off_bc, sb) : 0.0f;
       cv[i] = ok ? Elem<IO>::template load<0>(rc, off_bc, sb) : 0.0f;
     }
