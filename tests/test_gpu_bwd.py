@@ -151,3 +151,29 @@ def test_bwd_headline_shape():
     worst = {k: rel_err(g[k], r[k]) for k in GRADS if r.get(k) is not None and g.get(k) is not None}
     print("headline", " ".join(f"{k} {v:.1e}" for k, v in worst.items()), flush=True)
     assert all(v <= 2e-2 for v in worst.values()), worst
+
+
+def test_bwd_empty_and_degenerate():
+    """seqlen 0: the initial state's gradient is dh_last and every other one is
+    zero; batch 0 is a no-op; a single 16-channel group works."""
+    import torch
+    import selective_state_space_scan_amd as ssm
+    dev = torch.device("cuda:0")
+    nb, nd, N = 2, 32, 16
+    x = torch.empty((nb, 0, nd), dtype=torch.bfloat16, device=dev)
+    Bt = torch.empty((nb, 0, N), dtype=torch.bfloat16, device=dev)
+    A_log = torch.zeros((nd, N), device=dev)
+    D = torch.ones(nd, device=dev)
+    dhl = torch.randn((nb, nd, N), device=dev)
+    g = ssm.selective_scan_bwd(x, x, A_log, Bt, Bt, D, None, x, None, dh_last=dhl,
+                               delta_bias=torch.zeros(nd, device=dev))
+    torch.cuda.synchronize()
+    assert torch.equal(g["dh0"], dhl)
+    assert torch.all(g["dA_log"] == 0) and torch.all(g["dD"] == 0) and torch.all(g["ddelta_bias"] == 0)
+    x0 = torch.empty((0, 10, nd), dtype=torch.bfloat16, device=dev)
+    B0 = torch.empty((0, 10, N), dtype=torch.bfloat16, device=dev)
+    g0 = ssm.selective_scan_bwd(x0, x0, A_log, B0, B0, D, None, x0, None)
+    torch.cuda.synchronize()
+    assert g0["dx"].shape == (0, 10, nd)
+    w, inp = _case("f32", 16, 77, 1, 16, seed=23)
+    _compare(_gpu(inp, "f32"), _oracle(inp), 1e-4, "one group")
