@@ -86,6 +86,9 @@ struct FwdParams {
 // dstate 32 and 64 spill a few registers per tile to get there (measured: the
 // second workgroup per CU is worth far more than the spills cost).
 constexpr int kMinWavesPerSimd = 4;
+// The fold kernel keeps no Abar cache (~80 VGPRs) and one record buffer, so
+// three 8-wave workgroups share a CU.
+constexpr int kFoldWavesPerSimd = 6;
 
 // FOLD: the fold kernel of the time split -- pass 1 and the carry walk only,
 // over parts 0 .. n_parts-2, leaving each part's carry-out (part 0, from h0)
@@ -93,7 +96,7 @@ constexpr int kMinWavesPerSimd = 4;
 // Otherwise the full forward over every part, each starting from the state
 // the workspace gives for its first step.
 template <typename IO, int G, int K, int W, bool SOFTPLUS, bool CLAMP, bool GATE, bool FOLD>
-__global__ __launch_bounds__(64 * W, kMinWavesPerSimd) void ssm_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(64 * W, FOLD ? kFoldWavesPerSimd : kMinWavesPerSimd) void ssm_fwd_kernel(FwdParams p) {
   constexpr int N = 16 * G;             // states per channel
   constexpr int QR = 4 / G;             // time sub-chunks per wave
   constexpr int SUB = W * QR;           // sub-chunks per tile
@@ -114,10 +117,13 @@ __global__ __launch_bounds__(64 * W, kMinWavesPerSimd) void ssm_fwd_kernel(FwdPa
   // both touch 64 consecutive dwords (no bank conflicts).  Two buffers
   // alternate between tiles, so the next tile's pass 1 may write while the
   // previous one is still being read.
-  __shared__ __attribute__((aligned(16))) float agg_b[2][AGG];
+  // (The fold kernel has no pass 2 and uses one buffer, with a barrier after
+  // the walk instead.)
+  constexpr int NBUF = FOLD ? 1 : 2;
+  __shared__ __attribute__((aligned(16))) float agg_b[NBUF][AGG];
   // Sum of delta over each sub-chunk, channel-major (row stride SDS) so that a
   // walk lane reads its channel's sub-chunks as consecutive quads.
-  __shared__ __attribute__((aligned(16))) float agg_sd[2][16 * SDS];
+  __shared__ __attribute__((aligned(16))) float agg_sd[NBUF][16 * SDS];
   __shared__ __attribute__((aligned(16))) float a2s[16 * NS];  // A * log2(e) for the workgroup's channels
 
   // Workgroup -> (time part, batch row, channel group).  Workgroups are dealt
@@ -370,7 +376,10 @@ __global__ __launch_bounds__(64 * W, kMinWavesPerSimd) void ssm_fwd_kernel(FwdPa
         carry[k] = cr;
       }
     }
-    if constexpr (FOLD) return;  // the next tile's pass 1 writes the other record buffer
+    if constexpr (FOLD) {
+      __syncthreads();  // the next tile's pass 1 rewrites the single record buffer
+      return;
+    }
     if (want_chunks) {
       // The state after sub-chunk jj is the one the walk left for sub-chunk
       // jj + 1 (this lane's own LDS writes), or the carry after the last.
@@ -434,7 +443,8 @@ __global__ __launch_bounds__(64 * W, kMinWavesPerSimd) void ssm_fwd_kernel(FwdPa
   float xa[K], da[K], xn[K], dn[K];
   if (nfull > 0) load_xd.template operator()<true>(0, xa, da);
   for (int64_t tile = 0; tile < nfull; ++tile) {
-    tile_body.template operator()<true>(tile * T, static_cast<int>(tile & 1), xa, da, tile + 1 < nfull, xn, dn);
+    tile_body.template operator()<true>(tile * T, FOLD ? 0 : static_cast<int>(tile & 1), xa, da, tile + 1 < nfull,
+                                        xn, dn);
 #pragma unroll
     for (int i = 0; i < K; ++i) {
       xa[i] = xn[i];
@@ -444,7 +454,7 @@ __global__ __launch_bounds__(64 * W, kMinWavesPerSimd) void ssm_fwd_kernel(FwdPa
   int64_t t_next = nfull * T;
   if (t_next < len) {
     load_xd.template operator()<false>(t_next, xa, da);
-    tile_body.template operator()<false>(t_next, static_cast<int>(nfull & 1), xa, da, false, xn, dn);
+    tile_body.template operator()<false>(t_next, FOLD ? 0 : static_cast<int>(nfull & 1), xa, da, false, xn, dn);
     t_next += T;
   }
   if constexpr (FOLD) {
