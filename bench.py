@@ -56,14 +56,17 @@ FLOPEQ_BWD_PER_UPDATE = 32.0
 FLOPEQ_BWD_PER_ROW_STEP = 54.0
 
 PROFILES = os.path.join(HERE, "profiles")
-# The forward kernel's sources: a traffic record applies only to the build it was taken on.
-KERNEL_SRCS = [os.path.join(HERE, "selective_state_space_scan_amd", "csrc", f) for f in ("ssm_scan.hip", "ssm_internal.h")]
+# Each pass's kernel sources: a traffic record applies only to the build it was taken on.
+_CSRC = os.path.join(HERE, "selective_state_space_scan_amd", "csrc")
+KERNEL_SRCS = [os.path.join(_CSRC, f) for f in ("ssm_scan.hip", "ssm_internal.h")]
+BWD_KERNEL_SRCS = [os.path.join(_CSRC, f) for f in ("ssm_scan_bwd.hip", "ssm_internal.h")]
+TRAFFIC_RECORDS = {"fwd": ("ssm_fwd_kernel", KERNEL_SRCS), "bwd": ("ssm_bwd_kernel", BWD_KERNEL_SRCS)}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(srcs=KERNEL_SRCS) -> str:
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SRCS:
+    for f in srcs:
         h.update(open(f, "rb").read())
     return h.hexdigest()
 
@@ -94,12 +97,14 @@ def algorithmic_bytes_bwd(w, e: int, chunk_len: int) -> int:
             + 2 * w.dim * 4 + 2 * bdn * 4)
 
 
-def measured_traffic(w):
-    """HBM bytes per launch measured with rocprofv3 (FETCH_SIZE + WRITE_SIZE,
-    each scaled by the copy-kernel calibration) as recorded in profiles/, or
-    None when there is no record for this workload or the kernel source has
-    changed since it was taken."""
-    path = os.path.join(PROFILES, f"traffic_ssm_fwd_kernel_{w.name}.txt")
+def measured_traffic(w, kind: str = "fwd"):
+    """HBM bytes per launch of the pass `kind` ("fwd" or "bwd", the backward
+    counting its main and reduce kernels) measured with rocprofv3 (FETCH_SIZE +
+    WRITE_SIZE, each scaled by the copy-kernel calibration) as recorded in
+    profiles/, or None when there is no record for this workload or the
+    kernel source has changed since it was taken."""
+    kname, srcs = TRAFFIC_RECORDS[kind]
+    path = os.path.join(PROFILES, f"traffic_{kname}_{w.name}.txt")
     if not os.path.exists(path):
         return None
     rec = {}
@@ -107,12 +112,19 @@ def measured_traffic(w):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             rec[k.strip()] = v.strip()
-    if rec.get("kernel_source_sha256") != kernel_source_hash():
+    if rec.get("kernel_source_sha256") != kernel_source_hash(srcs):
         return None
     try:
         return int(float(rec["hbm_bytes_per_launch"]))
     except (KeyError, ValueError):
         return None
+
+
+def kernel_percentiles(kern_ms) -> dict:
+    """p10 / median / p90 of the per-launch kernel times (ms)."""
+    p = np.percentile(np.asarray(kern_ms, dtype=np.float64), [10, 50, 90])
+    return {"kernel_ms_p10": round(float(p[0]), 5), "kernel_ms_p50": round(float(p[1]), 5),
+            "kernel_ms_p90": round(float(p[2]), 5)}
 
 
 def cpu_baseline(inp, w, threads: int, min_seconds: float = 1.0) -> dict:
@@ -246,6 +258,7 @@ def main() -> int:
     roof["kernel"] = ("ssm_fwd_kernel" if parts == 1 else
                       f"ssm_fwd_kernel: fold of {parts - 1} time parts, then the forward over {parts} parts")
     roof["kernel_avg_ms"] = round(kern_avg_ms, 5)
+    roof.update(kernel_percentiles(kern_ms))
     roof["hbm_gbps"] = round(gbps, 1)
     roof["hbm_frac"] = round(gbps / HBM_PEAK_GBPS, 4)
     roof["algorithmic_bytes"] = nbytes
@@ -350,7 +363,8 @@ def bench_bwd(args, w, inp) -> int:
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_per_step = t_start.elapsed_time(t_end) / args.steps
-    kern_avg_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    kern_ms = [a.elapsed_time(b) for a, b in ev]
+    kern_avg_ms = float(np.mean(kern_ms))
     steps_valid = w.batch * w.seqlen if inp["valid_len"] is None else int(np.sum(inp["valid_len"]))
     updates = steps_valid * w.dim * w.dstate
     e = 2 if w.io == "bf16" else 4
@@ -358,15 +372,17 @@ def bench_bwd(args, w, inp) -> int:
     flops = steps_valid * w.dim * (w.dstate * FLOPEQ_BWD_PER_UPDATE + FLOPEQ_BWD_PER_ROW_STEP)
     gbps = nbytes / (kern_avg_ms * 1e-3) / 1e9
     tflops = flops / (kern_avg_ms * 1e-3) / 1e12
+    traffic = measured_traffic(w, "bwd")
     if flops / (FP32_VECTOR_PEAK_TFLOPS * 1e12) >= nbytes / (HBM_PEAK_GBPS * 1e9):
         roof = {"bound": "alu", "achieved": round(tflops, 3), "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(tflops / FP32_VECTOR_PEAK_TFLOPS, 4), "traffic": None}
+                "frac": round(tflops / FP32_VECTOR_PEAK_TFLOPS, 4), "traffic": traffic}
     else:
         roof = {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None}
+                "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic}
     roof.update({"kernel": "ssm_bwd_kernel + ssm_bwd_reduce_kernel", "kernel_avg_ms": round(kern_avg_ms, 5),
                  "hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes": nbytes,
                  "algorithmic_tflop": flops / 1e12, "traffic_unit": "bytes per launch"})
+    roof.update(kernel_percentiles(kern_ms))
     out = {
         "metric": "selective-scan backward state-updates/s (B·L·D·N) + HBM GB/s",
         "value": updates / (ms_per_step * 1e-3),

@@ -38,6 +38,11 @@
  * the io dtype with round-to-nearest-even.  Results are bitwise reproducible
  * run to run for the same inputs and dims.
  *
+ * Streams and graphs: a call only enqueues kernels on the caller's stream (no
+ * copies, memsets, allocations or synchronisation), so it may be captured
+ * into a HIP graph; a replay computes what the call would compute with the
+ * buffers' contents at replay time.
+ *
  * Errors: every entry point returns SSM_OK (0) or a negative SSM_ERR_* code and
  * never throws.  Argument checks happen on the host before anything is
  * enqueued; a failed check enqueues nothing.

@@ -134,6 +134,11 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
   constexpr int NT = 64 * W;
   constexpr int PPL = (PAIRS + NT - 1) / NT;
   constexpr int E = Elem<IO>::kBytes;
+  // Staging row blocks are 16 channels x 16 states, padded to 272 floats so
+  // that consecutive row blocks start 16 banks apart.
+  constexpr int RBS = 272;
+  constexpr int STG = (NT / 16) * RBS;
+  constexpr int REC = AGG > STG ? AGG : STG;
   static_assert(SUB % 4 == 0, "sub-chunk records are read as quads");
   static_assert(SUB * G * 16 == NT, "one reducing thread per (16-lane row, state)");
 
@@ -142,12 +147,12 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
   // state entering the sub-chunk; agg_m: reverse fold m, then mu at the
   // sub-chunk's end.  After pass 2 has read both, the two buffers stage the
   // dB / dC contributions for the sums over channels.
-  __shared__ __attribute__((aligned(16))) float agg_b[AGG];
-  __shared__ __attribute__((aligned(16))) float agg_m[AGG];
+  __shared__ __attribute__((aligned(16))) float agg_b[REC];
+  __shared__ __attribute__((aligned(16))) float agg_m[REC];
   __shared__ __attribute__((aligned(16))) float agg_sd[16 * SDS];
   __shared__ __attribute__((aligned(16))) float a2s[16 * NS];
   // Staging of step 0's dB / dC contributions (step 1's go to agg_b / agg_m).
-  __shared__ __attribute__((aligned(16))) float stg[2][AGG];
+  __shared__ __attribute__((aligned(16))) float stg[2][STG];
   __shared__ float red[2][NT];  // end of kernel: dD and dbias per lane
 
   const int64_t groups = static_cast<int64_t>(p.nb) * p.n_cg;
@@ -445,11 +450,14 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
     }
 
     // Staging for the sums over the 16 channels of a row: row block rb =
-    // j * G + g (SUB * G = NT / 16 of them) holds [c][s], 16 floats per lane
-    // written as quads; quad q of lane c sits at quad slot q ^ (rb % 4), so
-    // that the reducing threads of four row blocks (one wave) reading the same
-    // (c, s) hit four different banks.
+    // j * G + g (SUB * G = NT / 16 of them, RBS floats apart) holds [c][s],
+    // 16 floats per lane written as quads; quad q of lane c sits at quad slot
+    // q ^ swz(c), swz(c) = ((c3 ^ c1) << 1) | c2 for the bits of c.  Then the
+    // 16 lanes of a row write 64 distinct banks (any 8 of them, 32 distinct
+    // banks), and the reducing threads of the four row blocks of a wave, which
+    // read one channel each, hit four different 16-bank groups.
     const int rb = j * G + g;
+    const int csw = ((((c >> 3) ^ (c >> 1)) & 1) << 1) | ((c >> 2) & 1);
 #pragma unroll
     for (int ii = 0; ii < K; ++ii) {
       const int i = K - 1 - ii;  // steps in reverse
@@ -488,11 +496,11 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
         mu[s] = ab[i][s] * mu[s];
       }
       {
-        float* pbs = (i == 1 ? agg_b : stg[0]) + rb * 256 + c * 16;
-        float* pcs = (i == 1 ? agg_m : stg[1]) + rb * 256 + c * 16;
+        float* pbs = (i == 1 ? agg_b : stg[0]) + rb * RBS + c * 16;
+        float* pcs = (i == 1 ? agg_m : stg[1]) + rb * RBS + c * 16;
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
-          const int slot = (q4 ^ (rb & 3)) * 4;
+          const int slot = (q4 ^ csw) * 4;
           *reinterpret_cast<float4*>(pbs + slot) = make_float4(vb[4 * q4], vb[4 * q4 + 1], vb[4 * q4 + 2], vb[4 * q4 + 3]);
           *reinterpret_cast<float4*>(pcs + slot) = make_float4(vc[4 * q4], vc[4 * q4 + 1], vc[4 * q4 + 2], vc[4 * q4 + 3]);
         }
@@ -524,15 +532,15 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
     {
       // thread (rr, ss) sums the 16 channels of row block rr for state ss, both steps
       const int rr = tid >> 4, ss = tid & 15;
-      const int off = rr * 256 + (((ss >> 2) ^ (rr & 3)) * 4) + (ss & 3);
       float sb1 = 0.0f, sc1 = 0.0f, sb0 = 0.0f, sc0 = 0.0f;
-#pragma unroll
-      for (int cc = 0; cc < 16; ++cc) {
-        sb1 += agg_b[off + cc * 16];
-        sc1 += agg_m[off + cc * 16];
-        sb0 += stg[0][off + cc * 16];
-        sc0 += stg[1][off + cc * 16];
-      }
+      Unroll<0, 16>::run([&]<int CC>() {
+        constexpr int kSw = ((((CC >> 3) ^ (CC >> 1)) & 1) << 1) | ((CC >> 2) & 1);
+        const int off = rr * RBS + CC * 16 + (((ss >> 2) ^ kSw) * 4) + (ss & 3);
+        sb1 += agg_b[off];
+        sc1 += agg_m[off];
+        sb0 += stg[0][off];
+        sc0 += stg[1][off];
+      });
       const int jr = rr / G, gr = rr % G;
       const int64_t t0 = t_tile + jr * K;
       const int n = 16 * gr + ss;
@@ -731,9 +739,12 @@ int64_t bwd_ws_floats(int64_t nb, int64_t L, int64_t nd, int64_t N) {
          (kBwdMaxParts - 1) * (nb * nd * N + nb * nd);
 }
 
-__global__ void zero_fill_kernel(float* dst, int64_t n) {
+// dst[i] = src[i], or 0 with no src: the outputs of a call with no time
+// steps.  A kernel rather than a runtime copy or memset, so that a captured
+// call holds kernel nodes only.
+__global__ void copy_or_zero_kernel(float* dst, const float* src, int64_t n) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (i < n) dst[i] = 0.0f;
+  if (i < n) dst[i] = src != nullptr ? src[i] : 0.0f;
 }
 
 }  // namespace
@@ -881,22 +892,13 @@ int ssm_selective_scan_bwd(ssm_scan_t handle, const void* x, const void* delta, 
   if (L == 0) {
     // No steps: the adjoint of the initial state is dh_last; every other
     // gradient is zero.
-    const int64_t nz = nd * N + 2 * nd;
-    float* outs[] = {io->dA_log, io->dD, io->ddelta_bias};
-    const int64_t cnt[] = {nd * N, nd, nd};
-    (void)nz;
-    for (int k = 0; k < 3; ++k)
+    float* outs[] = {io->dA_log, io->dD, io->ddelta_bias, io->dh0};
+    const float* srcs[] = {nullptr, nullptr, nullptr, io->dh_last};
+    const int64_t cnt[] = {nd * N, nd, nd, nb * nd * N};
+    for (int k = 0; k < 4; ++k)
       if (outs[k] != nullptr)
-        hipLaunchKernelGGL(zero_fill_kernel, dim3(static_cast<unsigned>((cnt[k] + 255) / 256)), dim3(256), 0, s,
-                           outs[k], cnt[k]);
-    if (io->dh0 != nullptr) {
-      const int64_t n = nb * nd * N;
-      if (io->dh_last != nullptr)
-        (void)hipMemcpyAsync(io->dh0, io->dh_last, static_cast<size_t>(n) * 4, hipMemcpyDeviceToDevice, s);
-      else
-        hipLaunchKernelGGL(zero_fill_kernel, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, s, io->dh0,
-                           n);
-    }
+        hipLaunchKernelGGL(copy_or_zero_kernel, dim3(static_cast<unsigned>((cnt[k] + 255) / 256)), dim3(256), 0, s,
+                           outs[k], srcs[k], cnt[k]);
     return hipGetLastError() == hipSuccess ? SSM_OK : SSM_ERR_HIP;
   }
   // Eight-wave workgroups when the (row, channel group) grid leaves CUs idle
