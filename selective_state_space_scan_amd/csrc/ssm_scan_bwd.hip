@@ -134,25 +134,17 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
   constexpr int NT = 64 * W;
   constexpr int PPL = (PAIRS + NT - 1) / NT;
   constexpr int E = Elem<IO>::kBytes;
-  // Staging row blocks are 16 channels x 16 states, padded to 272 floats so
-  // that consecutive row blocks start 16 banks apart.
-  constexpr int RBS = 272;
-  constexpr int STG = (NT / 16) * RBS;
-  constexpr int REC = AGG > STG ? AGG : STG;
   static_assert(SUB % 4 == 0, "sub-chunk records are read as quads");
-  static_assert(SUB * G * 16 == NT, "one reducing thread per (16-lane row, state)");
+  static_assert(SUB * G * 16 == NT, "one lane per (sub-chunk, state group, channel)");
 
   // Sub-chunk records, float4 quads as in the forward: index
   // ((j * N/4 + n/4) * 16 + c) * 4 + n%4.  agg_b: forward b_total, then the
   // state entering the sub-chunk; agg_m: reverse fold m, then mu at the
-  // sub-chunk's end.  After pass 2 has read both, the two buffers stage the
-  // dB / dC contributions for the sums over channels.
-  __shared__ __attribute__((aligned(16))) float agg_b[REC];
-  __shared__ __attribute__((aligned(16))) float agg_m[REC];
+  // sub-chunk's end.  After the last tile agg_b stages the dA sums.
+  __shared__ __attribute__((aligned(16))) float agg_b[AGG];
+  __shared__ __attribute__((aligned(16))) float agg_m[AGG];
   __shared__ __attribute__((aligned(16))) float agg_sd[16 * SDS];
   __shared__ __attribute__((aligned(16))) float a2s[16 * NS];
-  // Staging of step 0's dB / dC contributions (step 1's go to agg_b / agg_m).
-  __shared__ __attribute__((aligned(16))) float stg[2][STG];
   __shared__ float red[2][NT];  // end of kernel: dD and dbias per lane
 
   const int64_t groups = static_cast<int64_t>(p.nb) * p.n_cg;
@@ -439,7 +431,7 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
         mu[s + 3] = m.w;
       }
     }
-    __syncthreads();  // agg_b / agg_m become the staging area below
+    __syncthreads();  // every wave has read its records: the next tile's pass 1 may overwrite them
 
     float hm[16];  // state after step 0
     {
@@ -449,15 +441,6 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
       Unroll<0, 16>::run([&]<int S>() { hm[S] = __builtin_fmaf(ab[0][S], hp[S], row_bcast<S>(b0) * u0); });
     }
 
-    // Staging for the sums over the 16 channels of a row: row block rb =
-    // j * G + g (SUB * G = NT / 16 of them, RBS floats apart) holds [c][s],
-    // 16 floats per lane written as quads; quad q of lane c sits at quad slot
-    // q ^ swz(c), swz(c) = ((c3 ^ c1) << 1) | c2 for the bits of c.  Then the
-    // 16 lanes of a row write 64 distinct banks (any 8 of them, 32 distinct
-    // banks), and the reducing threads of the four row blocks of a wave, which
-    // read one channel each, hit four different 16-bank groups.
-    const int rb = j * G + g;
-    const int csw = ((((c >> 3) ^ (c >> 1)) & 1) << 1) | ((c >> 2) & 1);
 #pragma unroll
     for (int ii = 0; ii < K; ++ii) {
       const int i = K - 1 - ii;  // steps in reverse
@@ -495,15 +478,14 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
         vc[s] = yi * hn[s];
         mu[s] = ab[i][s] * mu[s];
       }
-      {
-        float* pbs = (i == 1 ? agg_b : stg[0]) + rb * RBS + c * 16;
-        float* pcs = (i == 1 ? agg_m : stg[1]) + rb * RBS + c * 16;
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4) {
-          const int slot = (q4 ^ csw) * 4;
-          *reinterpret_cast<float4*>(pbs + slot) = make_float4(vb[4 * q4], vb[4 * q4 + 1], vb[4 * q4 + 2], vb[4 * q4 + 3]);
-          *reinterpret_cast<float4*>(pcs + slot) = make_float4(vc[4 * q4], vc[4 * q4 + 1], vc[4 * q4 + 2], vc[4 * q4 + 3]);
-        }
+      // dB, dC at this step: sums over the 16 channels of the row (lane c
+      // gets state 16 g + c)
+      const float sB = row_reduce_scatter16(vb, c);
+      const float sC = row_reduce_scatter16(vc, c);
+      if (i < left) {
+        const int64_t t = t_tile + j * K + i;
+        wdB[t * N + 16 * g + c] = sB;
+        wdC[t * N + 16 * g + c] = sC;
       }
       const float sgb = sum_state_groups<G>((sg4[0] + sg4[1]) + (sg4[2] + sg4[3]));
       const float sda = sum_state_groups<G>((sda4[0] + sda4[1]) + (sda4[2] + sda4[3]));
@@ -528,32 +510,6 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
         if constexpr (GATE) Elem<IO>::store(rdz, off_xd, sx, 0.0f);
       }
     }
-    __syncthreads();
-    {
-      // thread (rr, ss) sums the 16 channels of row block rr for state ss, both steps
-      const int rr = tid >> 4, ss = tid & 15;
-      float sb1 = 0.0f, sc1 = 0.0f, sb0 = 0.0f, sc0 = 0.0f;
-      Unroll<0, 16>::run([&]<int CC>() {
-        constexpr int kSw = ((((CC >> 3) ^ (CC >> 1)) & 1) << 1) | ((CC >> 2) & 1);
-        const int off = rr * RBS + CC * 16 + (((ss >> 2) ^ kSw) * 4) + (ss & 3);
-        sb1 += agg_b[off];
-        sc1 += agg_m[off];
-        sb0 += stg[0][off];
-        sc0 += stg[1][off];
-      });
-      const int jr = rr / G, gr = rr % G;
-      const int64_t t0 = t_tile + jr * K;
-      const int n = 16 * gr + ss;
-      if (t0 < len) {
-        wdB[t0 * N + n] = sb0;
-        wdC[t0 * N + n] = sc0;
-      }
-      if (t0 + 1 < len) {
-        wdB[(t0 + 1) * N + n] = sb1;
-        wdC[(t0 + 1) * N + n] = sc1;
-      }
-    }
-    __syncthreads();  // the next tile's pass 1 overwrites agg_b / agg_m
   }
 
   if constexpr (FOLD) {
