@@ -117,6 +117,67 @@ int64_t bwd_tile(int64_t N) {
 
 __device__ __forceinline__ float sigmoid_f32(float v) { return __builtin_amdgcn_rcpf(1.0f + fast_exp2(-v * kLog2e)); }
 
+// Reduce-scatter over the 16 lanes of a DPP row: every lane holds v[0..15];
+// lane c of the row gets the sum over the row's 16 lanes of their v[c].  A
+// four-level butterfly: at each level a lane keeps the half of its values
+// whose index bit matches its own lane bit and adds its partner's copy of
+// that half, the partner being lane c ^ 8 (row_ror:8), the mirror lane within
+// the 8-lane half (row_half_mirror; differs in bit 2), then c ^ 2 and c ^ 1
+// (quad_perm).  The first two levels pick the kept half per group of four
+// lanes with bank_mask, two masked DPP adds writing complementary lanes of
+// one register, so they need no selects; the last two select with
+// v_cndmask.  The order of the additions depends only on lane positions.
+// The leading s_nop covers the DPP hazards as in dot16_row_bcast; the early
+// clobbers keep the outputs out of the inputs' registers, since the first
+// masked add of each pair writes its output before the block has read every
+// input.  `c` is the lane's position in its row.
+__device__ __forceinline__ float row_reduce_scatter16(const float (&v)[16], int c) {
+  float h[8], q[4];
+  asm volatile(
+      "s_nop 4\n\t"
+      "v_add_f32_dpp %0, %8, %8 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %0, %16, %16 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %1, %9, %9 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %1, %17, %17 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %2, %10, %10 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %2, %18, %18 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %3, %11, %11 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %3, %19, %19 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %4, %12, %12 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %4, %20, %20 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %5, %13, %13 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %5, %21, %21 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %6, %14, %14 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %6, %22, %22 row_ror:8 row_mask:0xf bank_mask:0xc\n\t"
+      "v_add_f32_dpp %7, %15, %15 row_ror:8 row_mask:0xf bank_mask:0x3\n\t"
+      "v_add_f32_dpp %7, %23, %23 row_ror:8 row_mask:0xf bank_mask:0xc"
+      : "=&v"(h[0]), "=&v"(h[1]), "=&v"(h[2]), "=&v"(h[3]), "=&v"(h[4]), "=&v"(h[5]), "=&v"(h[6]), "=&v"(h[7])
+      : "v"(v[0]), "v"(v[1]), "v"(v[2]), "v"(v[3]), "v"(v[4]), "v"(v[5]), "v"(v[6]), "v"(v[7]), "v"(v[8]),
+        "v"(v[9]), "v"(v[10]), "v"(v[11]), "v"(v[12]), "v"(v[13]), "v"(v[14]), "v"(v[15]));
+  asm volatile(
+      "s_nop 4\n\t"
+      "v_add_f32_dpp %0, %4, %4 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
+      "v_add_f32_dpp %0, %8, %8 row_half_mirror row_mask:0xf bank_mask:0xa\n\t"
+      "v_add_f32_dpp %1, %5, %5 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
+      "v_add_f32_dpp %1, %9, %9 row_half_mirror row_mask:0xf bank_mask:0xa\n\t"
+      "v_add_f32_dpp %2, %6, %6 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
+      "v_add_f32_dpp %2, %10, %10 row_half_mirror row_mask:0xf bank_mask:0xa\n\t"
+      "v_add_f32_dpp %3, %7, %7 row_half_mirror row_mask:0xf bank_mask:0x5\n\t"
+      "v_add_f32_dpp %3, %11, %11 row_half_mirror row_mask:0xf bank_mask:0xa"
+      : "=&v"(q[0]), "=&v"(q[1]), "=&v"(q[2]), "=&v"(q[3])
+      : "v"(h[0]), "v"(h[1]), "v"(h[2]), "v"(h[3]), "v"(h[4]), "v"(h[5]), "v"(h[6]), "v"(h[7]));
+  // c ^ 2: keep q[0..1] (bit 1 clear) or q[2..3]
+  const bool b1 = (c & 2) != 0, b0 = (c & 1) != 0;
+  auto xchg = []<int CTRL>(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+  };
+  constexpr int kXor2 = 0x4e, kXor1 = 0xb1;  // quad_perm [2,3,0,1] and [1,0,3,2]
+  const float r0 = (b1 ? q[2] : q[0]) + xchg.template operator()<kXor2>(b1 ? q[0] : q[2]);
+  const float r1 = (b1 ? q[3] : q[1]) + xchg.template operator()<kXor2>(b1 ? q[1] : q[3]);
+  // c ^ 1
+  return (b0 ? r1 : r0) + xchg.template operator()<kXor1>(b0 ? r0 : r1);
+}
+
 // FOLD: the fold kernel of the time split (pass 1 and the reverse walk only,
 // over parts 1 .. n_parts-1).  Otherwise the backward over every part.
 template <typename IO, int G, int W, bool SOFTPLUS, bool CLAMP, bool GATE, bool FOLD>
