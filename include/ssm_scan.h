@@ -1,7 +1,8 @@
 /*
- * ssm_scan.h -- C ABI of the MI355X (gfx950) fused selective-scan forward.
+ * ssm_scan.h -- C ABI of the MI355X (gfx950) fused selective scan: the
+ * forward and its backward (ssm_selective_scan_bwd, further below).
  *
- * The operation (Mamba's selective state-space scan, forward only).  For every
+ * The operation (Mamba's selective state-space scan).  For every
  * batch row b, channel d and state n, with A = -exp(A_log[d,n]):
  *
  *     delta_t = softplus(delta_raw[b,t,d])            (optional; then optional clip)
@@ -63,7 +64,8 @@ enum ssm_io_dtype { SSM_IO_F32 = 0, SSM_IO_BF16 = 1 };
 enum ssm_status {
   SSM_OK = 0,
   SSM_ERR_INVALID_ARG = -1,     /* NULL required pointer or handle, negative dim, bad flag or clip bounds */
-  SSM_ERR_UNSUPPORTED = -2,     /* dstate not 16/32/64, dim not a multiple of 16, misaligned pointer, wrong GPU */
+  SSM_ERR_UNSUPPORTED = -2,     /* dstate not 16/32/64, dim not a multiple of 16, misaligned pointer, wrong GPU,
+                                   one batch row of x, delta, B or C over 2 GiB, or a grid too large */
   SSM_ERR_ALIAS = -3,           /* y or h_last overlaps an input, or y overlaps h_last */
   SSM_ERR_HIP = -4,             /* a HIP runtime or launch error */
   SSM_ERR_NO_DEVICE = -5,       /* no usable GPU at the requested ordinal */

@@ -1,9 +1,9 @@
-"""Fused selective state-space scan forward for MI355X (gfx950).
+"""Fused selective state-space scan, forward and backward, for MI355X (gfx950).
 
 The scan itself runs in the HIP library ``libssmscan.so`` behind the C ABI of
-``include/ssm_scan.h``; this package is its thin binding (``selective_scan_fwd``
-and the raw ``ssm_*`` calls), the build script and the seeded synthetic input
-generators.
+``include/ssm_scan.h``; this package is its thin binding (``selective_scan_fwd``,
+``selective_scan_bwd`` and the raw ``ssm_*`` calls), the build script and the
+seeded synthetic input generators.
 """
 from ._binding import (EXPORTED, SSM_ERR_ALIAS, SSM_ERR_DEVICE_MISMATCH, SSM_ERR_HIP, SSM_ERR_INVALID_ARG,
                        SSM_ERR_NO_DEVICE, SSM_ERR_UNSUPPORTED, SSM_IO_BF16, SSM_IO_F32, SSM_OK, SsmScanError,
