@@ -386,7 +386,8 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
         dyp[i] = dyv[i];
       }
     }
-    float ab[K][16];
+    // Abar and the input terms B u of both steps stay in registers for pass 2
+    float ab[K][16], bu[K][16];
     float bt[16], mm[16];
 #pragma unroll
     for (int i = 0; i < K; ++i) {
@@ -394,8 +395,10 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
       const float ui = u[i];
       Unroll<0, 16>::run([&]<int S>() {
         ab[i][S] = fast_exp2(dl[i] * A2[S]);
-        if constexpr (!FOLD)
-          bt[S] = (i == 0) ? row_bcast<S>(bi) * ui : __builtin_fmaf(ab[i][S], bt[S], row_bcast<S>(bi) * ui);
+        if constexpr (!FOLD) {
+          bu[i][S] = row_bcast<S>(bi) * ui;
+          bt[S] = (i == 0) ? bu[0][S] : __builtin_fmaf(ab[i][S], bt[S], bu[i][S]);
+        }
       });
     }
     {
@@ -495,12 +498,8 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
     __syncthreads();  // every wave has read its records: the next tile's pass 1 may overwrite them
 
     float hm[16];  // state after step 0
-    {
-      float b0 = bv[0];
-      asm volatile("" : "+v"(b0));
-      const float u0 = u[0];
-      Unroll<0, 16>::run([&]<int S>() { hm[S] = __builtin_fmaf(ab[0][S], hp[S], row_bcast<S>(b0) * u0); });
-    }
+#pragma unroll
+    for (int s = 0; s < 16; ++s) hm[s] = __builtin_fmaf(ab[0][s], hp[s], bu[0][s]);
 
 #pragma unroll
     for (int ii = 0; ii < K; ++ii) {
@@ -508,10 +507,8 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
       // the state after step i (hn) and the one before it (hb)
       float hn[16];
       if (i == 1) {
-        float b1 = bv[1];
-        asm volatile("" : "+v"(b1));
-        const float u1 = u[1];
-        Unroll<0, 16>::run([&]<int S>() { hn[S] = __builtin_fmaf(ab[1][S], hm[S], row_bcast<S>(b1) * u1); });
+#pragma unroll
+        for (int s = 0; s < 16; ++s) hn[s] = __builtin_fmaf(ab[1][s], hm[s], bu[1][s]);
       } else {
 #pragma unroll
         for (int s = 0; s < 16; ++s) hn[s] = hm[s];
@@ -532,12 +529,12 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
       float vb[16], vc[16];
 #pragma unroll
       for (int s = 0; s < 16; ++s) {
-        const float daa = mu[s] * hb[s] * ab[i][s];
-        sda4[s & 3] = __builtin_fmaf(daa, A2[s], sda4[s & 3]);
-        dAl[s] = __builtin_fmaf(daa, dl[i], dAl[s]);
         vb[s] = mu[s] * u[i];
         vc[s] = yi * hn[s];
-        mu[s] = ab[i][s] * mu[s];
+        mu[s] = ab[i][s] * mu[s];  // the adjoint before step i
+        const float daa = mu[s] * hb[s];
+        sda4[s & 3] = __builtin_fmaf(daa, A2[s], sda4[s & 3]);
+        dAl[s] = __builtin_fmaf(daa, dl[i], dAl[s]);
       }
       // dB, dC at this step: sums over the 16 channels of the row (lane c
       // gets state 16 g + c)
