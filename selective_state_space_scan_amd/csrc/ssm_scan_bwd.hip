@@ -401,12 +401,15 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
         }
       });
     }
+    // reverse fold over the K = 2 steps: m = Abar_0 (c_0 + Abar_1 c_1) with
+    // c = dyp C; pass 2 adds the same c terms to the adjoint
+    float cy[K][16];
     {
-      // reverse fold over the K = 2 steps: m = Abar_0 (c_0 + Abar_1 c_1)
       const float c0 = cv[0], c1 = cv[1], y0 = dyp[0], y1 = dyp[1];
       Unroll<0, 16>::run([&]<int S>() {
-        const float t1 = ab[1][S] * (row_bcast<S>(c1) * y1);
-        mm[S] = ab[0][S] * __builtin_fmaf(row_bcast<S>(c0), y0, t1);
+        cy[0][S] = row_bcast<S>(c0) * y0;
+        cy[1][S] = row_bcast<S>(c1) * y1;
+        mm[S] = ab[0][S] * __builtin_fmaf(ab[1][S], cy[1][S], cy[0][S]);
       });
     }
     {
@@ -516,7 +519,8 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
       const float(&hb)[16] = (i == 1) ? hm : hp;
       const float yi = dyp[i];
       // mu becomes the adjoint of the state after step i: mu + dyp * C
-      axpy16_row_bcast(mu, cv[i], yi);
+#pragma unroll
+      for (int s = 0; s < 16; ++s) mu[s] += cy[i][s];
       float sg4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
       dot16_row_bcast(sg4, bv[i], mu);  // sum_n g B
       float ypre = 0.0f;
