@@ -117,6 +117,20 @@ int64_t bwd_tile(int64_t N) {
 
 __device__ __forceinline__ float sigmoid_f32(float v) { return __builtin_amdgcn_rcpf(1.0f + fast_exp2(-v * kLog2e)); }
 
+// softplus(v) (as softplus_f32) and its derivative sigmoid(v) from one exp:
+// with e = exp(-|v|) and w = 1 + e, sigmoid(v) = 1 / w for v >= 0 and e / w
+// below.
+__device__ __forceinline__ float softplus_sigmoid_f32(float v, float& sig) {
+  const float e = fast_exp2(-__builtin_fabsf(v) * kLog2e);
+  const float w = 1.0f + e;
+  const float wm1 = w - 1.0f;
+  const float lg = __builtin_amdgcn_logf(w) * kLn2;
+  const float rw = __builtin_amdgcn_rcpf(w);
+  sig = (v >= 0.0f) ? rw : e * rw;
+  const float l1p = (wm1 == 0.0f) ? e : lg * (e * __builtin_amdgcn_rcpf(wm1));
+  return __builtin_fmaxf(v, 0.0f) + l1p;
+}
+
 // Reduce-scatter over the 16 lanes of a DPP row: every lane holds v[0..15];
 // lane c of the row gets the sum over the row's 16 lanes of their v[c].  A
 // four-level butterfly: at each level a lane keeps the half of its values
@@ -312,9 +326,31 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
 
   __syncthreads();  // a2s is written
 
+  // The state entering tile kt (h0, or the chunk state the forward saved) is
+  // loaded one tile ahead, so that its latency hides behind a whole tile --
+  // when a thread walks at most two pairs (dstate 16, 32); with four (dstate
+  // 64) the registers are not there, and it is loaded where the walk needs it.
+  constexpr bool kAhead = PPL <= 2;
+  auto load_h_in = [&](int64_t kt, int k) -> float {
+    const int64_t gt = tile0 + kt;
+    if (gt == 0) return (p.h0 != nullptr) ? p.h0[state_block + pair_offset(k)] : 0.0f;
+    return p.chunk_states[((static_cast<int64_t>(b) * p.n_chunks + gt * CS - 1) * nd + cg * 16) * N +
+                          pair_offset(k)];
+  };
+  float h_next[PPL];
+#pragma unroll
+  for (int k = 0; k < PPL; ++k)
+    h_next[k] = (kAhead && !FOLD && pair_valid(k) && n_tiles > 0) ? load_h_in(n_tiles - 1, k) : 0.0f;
+
   for (int64_t kt = n_tiles - 1; kt >= 0; --kt) {
     const int64_t t_tile = kt * T;
     const int64_t left = len - t_tile - j * K;  // valid steps from this lane's first step
+    float h_in[PPL];
+#pragma unroll
+    for (int k = 0; k < PPL; ++k) {
+      h_in[k] = h_next[k];
+      if (kAhead && !FOLD && pair_valid(k) && kt > 0) h_next[k] = load_h_in(kt - 1, k);
+    }
     if (len <= t_tile) {
       // A tile wholly in the padding: zero gradients, the adjoint passes through.
       if constexpr (FOLD) continue;
@@ -367,8 +403,7 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
       const float raw = dlr[i] + dbias;
       float v = raw, f = 1.0f;
       if constexpr (SOFTPLUS) {
-        v = softplus_f32(raw);
-        f = sigmoid_f32(raw);
+        v = softplus_sigmoid_f32(raw, f);
       }
       if constexpr (CLAMP) {
         f = (v >= p.dmin && v <= p.dmax) ? f : 0.0f;
@@ -451,14 +486,7 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
             part_sd[k] += (v.x + v.y) + (v.z + v.w);
           }
         } else {
-          // the state entering the tile: h0, or the chunk state the forward saved
-          const int64_t gt = tile0 + kt;
-          float h;
-          if (gt == 0)
-            h = (p.h0 != nullptr) ? p.h0[state_block + pair_offset(k)] : 0.0f;
-          else
-            h = p.chunk_states[((static_cast<int64_t>(b) * p.n_chunks + gt * CS - 1) * nd + cg * 16) * N +
-                               pair_offset(k)];
+          float h = kAhead ? h_in[k] : load_h_in(kt, k);  // the state entering the tile
 #pragma unroll
           for (int jj = 0; jj < SUB; ++jj) {
             const float bb = pbw[jj * (N / 4) * 64];
