@@ -157,6 +157,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", type=int, default=2, help="workload index (default: the headline one)")
     ap.add_argument("--rotate", type=int, default=3, help="input copies rotated between steps")
+    ap.add_argument("--time-parts", type=int, default=0,
+                    help="forward time split: parts to cut the sequence into (default 0: the library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (default: min(16, cpus))")
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
@@ -210,7 +212,7 @@ def main() -> int:
     dims = ssm.ssm_scan_dims()
     dims.batch, dims.seqlen, dims.dim, dims.dstate = w.batch, w.seqlen, w.dim, w.dstate
     dims.io_dtype = ssm.SSM_IO_BF16 if w.io == "bf16" else ssm.SSM_IO_F32
-    parts = ssm.auto_time_parts(ssm._binding.handle_for(dev.index or 0), dims)
+    parts = args.time_parts or ssm.auto_time_parts(ssm._binding.handle_for(dev.index or 0), dims)
     ws_bytes = ssm.workspace_bytes(dims, parts)
     ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
 

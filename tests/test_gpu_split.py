@@ -92,7 +92,7 @@ def test_auto_split_small_batch_long_sequence():
     dims = ssm.ssm_scan_dims()
     dims.batch, dims.seqlen, dims.dim, dims.dstate, dims.io_dtype = 1, 4096, 64, 64, ssm.SSM_IO_BF16
     parts = ssm.auto_time_parts(ssm._binding.handle_for(torch.cuda.current_device()), dims)
-    assert parts == 8
+    assert parts == 16
     y, h, cs = _run(inp, "bf16", None, clamp=(1e-3, 0.1))
     yr, hr, csr = oracle.selective_scan(inp["x"], inp["delta"], inp["A_log"], inp["B"], inp["C"], inp["D"],
                                         delta_clamp=(1e-3, 0.1), chunk_len=ssm.chunk_len(64), nthreads=8)
@@ -114,4 +114,4 @@ def test_headline_shape_is_not_split():
     w = I.WORKLOADS[4]
     dims = ssm.ssm_scan_dims()
     dims.batch, dims.seqlen, dims.dim, dims.dstate, dims.io_dtype = w.batch, w.seqlen, w.dim, w.dstate, 1
-    assert ssm.auto_time_parts(h, dims) == 8
+    assert ssm.auto_time_parts(h, dims) == 16
