@@ -364,6 +364,8 @@ def selective_scan_bwd(x, delta, A_log, B, C, D, valid_len, dy, chunk_states, *,
     if io is None or x.dim() != 3:
         raise ValueError("x must be a [batch, L, dim] float32 or bfloat16 tensor")
     nb, L, nd = x.shape
+    if A_log.dim() != 2 or A_log.shape[0] != nd:
+        raise ValueError("A_log must be [dim, dstate]")
     N = A_log.shape[1]
     for name, t, shape, dt in (("delta", delta, (nb, L, nd), x.dtype), ("B", B, (nb, L, N), x.dtype),
                                ("C", C, (nb, L, N), x.dtype), ("A_log", A_log, (nd, N), torch.float32),
@@ -373,7 +375,8 @@ def selective_scan_bwd(x, delta, A_log, B, C, D, valid_len, dy, chunk_states, *,
     cl = bwd_chunk_len(N)
     n_chunks = (L + cl - 1) // cl if cl > 0 else 0
     if chunk_states is not None and (tuple(chunk_states.shape) != (nb, n_chunks, nd, N)
-                                     or chunk_states.dtype != torch.float32 or not chunk_states.is_contiguous()):
+                                     or chunk_states.dtype != torch.float32 or chunk_states.device != dev
+                                     or not chunk_states.is_contiguous()):
         raise ValueError(f"chunk_states must be [batch, {n_chunks}, dim, dstate] float32 "
                          f"(the forward's, with chunk_len={cl})")
     for name, t, shape in (("dh_last", dh_last, (nb, nd, N)), ("h0", h0, (nb, nd, N)),
@@ -381,8 +384,12 @@ def selective_scan_bwd(x, delta, A_log, B, C, D, valid_len, dy, chunk_states, *,
         if t is not None and (tuple(t.shape) != shape or t.dtype != torch.float32 or t.device != dev
                               or not t.is_contiguous()):
             raise ValueError(f"{name} must be a contiguous {shape} float32 tensor on {dev}")
-    if z is not None and (tuple(z.shape) != (nb, L, nd) or z.dtype != x.dtype or not z.is_contiguous()):
+    if z is not None and (tuple(z.shape) != (nb, L, nd) or z.dtype != x.dtype or z.device != dev
+                          or not z.is_contiguous()):
         raise ValueError("z must be a contiguous tensor like x")
+    if valid_len is not None and (tuple(valid_len.shape) != (nb,) or valid_len.dtype != torch.int32
+                                  or valid_len.device != dev or not valid_len.is_contiguous()):
+        raise ValueError("valid_len must be a contiguous [batch] int32 tensor on x's device")
     out = dict(dx=torch.empty_like(x), ddelta=torch.empty_like(x), dz=torch.empty_like(x) if z is not None else None,
                dA_log=torch.empty((nd, N), dtype=torch.float32, device=dev),
                dB=torch.empty((nb, L, N), dtype=torch.float32, device=dev),
@@ -411,8 +418,9 @@ def selective_scan_bwd(x, delta, A_log, B, C, D, valid_len, dy, chunk_states, *,
         workspace = torch.empty(max(nbytes, 4), dtype=torch.uint8, device=dev)
         if hasattr(stream, "cuda_stream"):
             workspace.record_stream(stream)
-    elif workspace.dtype != torch.uint8 or workspace.numel() < nbytes or not workspace.is_contiguous():
-        raise ValueError(f"workspace must be a contiguous uint8 tensor of at least {nbytes} bytes")
+    elif (workspace.dtype != torch.uint8 or workspace.device != dev or workspace.numel() < nbytes
+          or not workspace.is_contiguous()):
+        raise ValueError(f"workspace must be a contiguous uint8 tensor of at least {nbytes} bytes on {dev}")
     extras = ssm_scan_fwd_extras(ptr(h0), ptr(delta_bias), ptr(z), None, 0, 0, None, 0)
     bio = ssm_scan_bwd_io(ptr(dy), ptr(dh_last), ptr(chunk_states), ptr(out["dx"]), ptr(out["ddelta"]),
                           ptr(out["dz"]), ptr(out["dA_log"]), ptr(out["dB"]), ptr(out["dC"]), ptr(out["dD"]),
