@@ -177,3 +177,28 @@ def test_bwd_empty_and_degenerate():
     assert g0["dx"].shape == (0, 10, nd)
     w, inp = _case("f32", 16, 77, 1, 16, seed=23)
     _compare(_gpu(inp, "f32"), _oracle(inp), 1e-4, "one group")
+
+
+def test_bwd_binding_rejects_bad_arguments():
+    """The binding's own checks raise before anything is enqueued."""
+    import torch
+    import selective_state_space_scan_amd as ssm
+    w, inp = _case("bf16", 16, 100, 2, 32, seed=77, extras=False)
+    dev = to_device(inp, "bf16")
+    dy = torch.from_numpy(inp["dy"]).cuda().to(torch.bfloat16)
+    _, _, cs = ssm.selective_scan_fwd(dev["x"], dev["delta"], dev["A_log"], dev["B"], dev["C"], dev["D"], None,
+                                      return_chunk_states=True, chunk_len=ssm.bwd_chunk_len(16))
+    args = (dev["x"], dev["delta"], dev["A_log"], dev["B"], dev["C"], dev["D"])
+    with pytest.raises(ValueError):
+        ssm.selective_scan_bwd(*args, torch.full((2,), 100, dtype=torch.int64, device="cuda"), dy, cs)
+    with pytest.raises(ValueError):
+        ssm.selective_scan_bwd(*args, None, dy, cs[:, :1].contiguous())
+    with pytest.raises(ValueError):
+        ssm.selective_scan_bwd(*args, None, dy, cs, z=dev["x"].float())
+    with pytest.raises(ValueError):
+        ssm.selective_scan_bwd(dev["x"], dev["delta"], dev["A_log"][:, 0].contiguous(), dev["B"], dev["C"],
+                               dev["D"], None, dy, cs)
+    torch.cuda.synchronize()
+    g = ssm.selective_scan_bwd(*args, None, dy, cs)  # and the good call still works
+    torch.cuda.synchronize()
+    assert torch.isfinite(g["dx"].float()).all()
