@@ -367,20 +367,30 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
     }
 
     // ---- loads ----
+    // A tile wholly inside the valid length (every one but the last) loads
+    // without per-lane conditions, so that its loads issue together instead
+    // of one masked branch (and one wait) per load.
+    const bool full = t_tile + T <= len;  // uniform over the workgroup
     float xv[K], dlr[K], dyv[K], zv[K], bv[K], cv[K];
+    auto load_tile = [&]<bool FULL>() {
 #pragma unroll
-    for (int i = 0; i < K; ++i) {
-      const bool ok = i < left;
-      const uint32_t sx = static_cast<uint32_t>((t_tile + i) * xd_step);
-      const uint32_t sb = static_cast<uint32_t>((t_tile + i) * bc_step);
-      // the fold needs neither x nor B (only the adjoint input dyp * C)
-      xv[i] = (ok && !FOLD) ? Elem<IO>::template load<kCached>(rx, off_xd, sx) : 0.0f;
-      dlr[i] = ok ? Elem<IO>::template load<kCached>(rd, off_xd, sx) : 0.0f;
-      dyv[i] = ok ? Elem<IO>::template load<kCached>(rdy, off_xd, sx) : 0.0f;
-      zv[i] = (GATE && ok) ? Elem<IO>::template load<kCached>(rz, off_xd, sx) : 0.0f;
-      bv[i] = (ok && !FOLD) ? Elem<IO>::template load<0>(rb, off_bc, sb) : 0.0f;
-      cv[i] = ok ? Elem<IO>::template load<0>(rc, off_bc, sb) : 0.0f;
-    }
+      for (int i = 0; i < K; ++i) {
+        const bool ok = FULL || i < left;
+        const uint32_t sx = static_cast<uint32_t>((t_tile + i) * xd_step);
+        const uint32_t sb = static_cast<uint32_t>((t_tile + i) * bc_step);
+        // the fold needs neither x nor B (only the adjoint input dyp * C)
+        xv[i] = (ok && !FOLD) ? Elem<IO>::template load<kCached>(rx, off_xd, sx) : 0.0f;
+        dlr[i] = ok ? Elem<IO>::template load<kCached>(rd, off_xd, sx) : 0.0f;
+        dyv[i] = ok ? Elem<IO>::template load<kCached>(rdy, off_xd, sx) : 0.0f;
+        zv[i] = (GATE && ok) ? Elem<IO>::template load<kCached>(rz, off_xd, sx) : 0.0f;
+        bv[i] = (ok && !FOLD) ? Elem<IO>::template load<0>(rb, off_bc, sb) : 0.0f;
+        cv[i] = ok ? Elem<IO>::template load<0>(rc, off_bc, sb) : 0.0f;
+      }
+    };
+    if (full)
+      load_tile.template operator()<true>();
+    else
+      load_tile.template operator()<false>();
     float A2[16];
     {
       const float* pa = a2s + c * NS + 16 * g;
