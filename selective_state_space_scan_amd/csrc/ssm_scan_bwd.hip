@@ -372,13 +372,30 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
     // of one masked branch (and one wait) per load.
     const bool full = t_tile + T <= len;  // uniform over the workgroup
     float xv[K], dlr[K], dyv[K], zv[K], bv[K], cv[K];
-    auto load_tile = [&]<bool FULL>() {
+    if (full) {
+      // (B and C first: a different order from the masked loads below keeps
+      // the compiler from merging the two paths' last loads into one block)
 #pragma unroll
       for (int i = 0; i < K; ++i) {
-        const bool ok = FULL || i < left;
+        const uint32_t sb = static_cast<uint32_t>((t_tile + i) * bc_step);
+        cv[i] = Elem<IO>::template load<0>(rc, off_bc, sb);
+        bv[i] = !FOLD ? Elem<IO>::template load<0>(rb, off_bc, sb) : 0.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < K; ++i) {
+        const uint32_t sx = static_cast<uint32_t>((t_tile + i) * xd_step);
+        // the fold needs neither x nor B (only the adjoint input dyp * C)
+        xv[i] = !FOLD ? Elem<IO>::template load<kCached>(rx, off_xd, sx) : 0.0f;
+        dlr[i] = Elem<IO>::template load<kCached>(rd, off_xd, sx);
+        dyv[i] = Elem<IO>::template load<kCached>(rdy, off_xd, sx);
+        zv[i] = GATE ? Elem<IO>::template load<kCached>(rz, off_xd, sx) : 0.0f;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < K; ++i) {
+        const bool ok = i < left;
         const uint32_t sx = static_cast<uint32_t>((t_tile + i) * xd_step);
         const uint32_t sb = static_cast<uint32_t>((t_tile + i) * bc_step);
-        // the fold needs neither x nor B (only the adjoint input dyp * C)
         xv[i] = (ok && !FOLD) ? Elem<IO>::template load<kCached>(rx, off_xd, sx) : 0.0f;
         dlr[i] = ok ? Elem<IO>::template load<kCached>(rd, off_xd, sx) : 0.0f;
         dyv[i] = ok ? Elem<IO>::template load<kCached>(rdy, off_xd, sx) : 0.0f;
@@ -386,11 +403,7 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
         bv[i] = (ok && !FOLD) ? Elem<IO>::template load<0>(rb, off_bc, sb) : 0.0f;
         cv[i] = ok ? Elem<IO>::template load<0>(rc, off_bc, sb) : 0.0f;
       }
-    };
-    if (full)
-      load_tile.template operator()<true>();
-    else
-      load_tile.template operator()<false>();
+    }
     float A2[16];
     {
       const float* pa = a2s + c * NS + 16 * g;
@@ -582,7 +595,7 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
       // gets state 16 g + c)
       const float sB = row_reduce_scatter16(vb, c);
       const float sC = row_reduce_scatter16(vc, c);
-      if (i < left) {
+      if (full || i < left) {
         const int64_t t = t_tile + j * K + i;
         wdB[t * N + 16 * g + c] = sB;
         wdC[t * N + 16 * g + c] = sC;
@@ -593,7 +606,7 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
       const float ddt = __builtin_fmaf(xv[i], sgb, sda * kLn2);  // A = A2 ln 2
       const float ddraw = ddt * fac[i];
       const float dxv = __builtin_fmaf(dl[i], sgb, yi * dskip);
-      if (i < left && (G == 1 || (i % G) == g)) {
+      if ((full || i < left) && (G == 1 || (i % G) == g)) {
         const uint32_t sx = static_cast<uint32_t>((t_tile + i) * xd_step);
         Elem<IO>::store(rdx, off_xd, sx, dxv);
         Elem<IO>::store(rdd, off_xd, sx, ddraw);
