@@ -327,9 +327,11 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
   __syncthreads();  // a2s is written
 
   // The state entering tile kt (h0, or the chunk state the forward saved) is
-  // loaded one tile ahead, so that its latency hides behind a whole tile --
+  // loaded at the top of the tile, so that its latency hides behind pass 1 --
   // when a thread walks at most two pairs (dstate 16, 32); with four (dstate
   // 64) the registers are not there, and it is loaded where the walk needs it.
+  // (Loading it a whole tile ahead costs a register copy at the loop's end,
+  // which waits for every outstanding memory operation, stores included.)
   constexpr bool kAhead = PPL <= 2;
   auto load_h_in = [&](int64_t kt, int k) -> float {
     const int64_t gt = tile0 + kt;
@@ -337,20 +339,10 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
     return p.chunk_states[((static_cast<int64_t>(b) * p.n_chunks + gt * CS - 1) * nd + cg * 16) * N +
                           pair_offset(k)];
   };
-  float h_next[PPL];
-#pragma unroll
-  for (int k = 0; k < PPL; ++k)
-    h_next[k] = (kAhead && !FOLD && pair_valid(k) && n_tiles > 0) ? load_h_in(n_tiles - 1, k) : 0.0f;
 
   for (int64_t kt = n_tiles - 1; kt >= 0; --kt) {
     const int64_t t_tile = kt * T;
     const int64_t left = len - t_tile - j * K;  // valid steps from this lane's first step
-    float h_in[PPL];
-#pragma unroll
-    for (int k = 0; k < PPL; ++k) {
-      h_in[k] = h_next[k];
-      if (kAhead && !FOLD && pair_valid(k) && kt > 0) h_next[k] = load_h_in(kt - 1, k);
-    }
     if (len <= t_tile) {
       // A tile wholly in the padding: zero gradients, the adjoint passes through.
       if constexpr (FOLD) continue;
@@ -367,6 +359,9 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
     }
 
     // ---- loads ----
+    float h_in[PPL];
+#pragma unroll
+    for (int k = 0; k < PPL; ++k) h_in[k] = (kAhead && !FOLD && pair_valid(k)) ? load_h_in(kt, k) : 0.0f;
     // A tile wholly inside the valid length (every one but the last) loads
     // without per-lane conditions, so that its loads issue together instead
     // of one masked branch (and one wait) per load.
