@@ -254,16 +254,25 @@ __global__ __launch_bounds__(64 * W, FOLD ? kFoldWavesPerSimd : kMinWavesPerSimd
   const uint32_t off_xd = static_cast<uint32_t>((j * K * nd + d) * E);
   const uint32_t off_bc = static_cast<uint32_t>((j * K * N + 16 * g + c) * E);
 
-  // x and delta of the lane's K steps in the tile starting at t_tile.  Steps
-  // at or beyond len read as 0 (never loaded).
-  auto load_xd = [&]<bool FULL>(int64_t t_tile, float (&xv)[K], float (&dv)[K]) {
+  // x and delta of the lane's K steps in the tile starting at t_tile, as the
+  // loaded bits (widened to fp32 where they are used, so that a prefetch does
+  // not wait for its data on the spot).  Steps at or beyond len read as 0
+  // (never loaded).
+  auto load_raw = [](rsrc_t r, uint32_t voff, uint32_t soff) -> uint32_t {
+    if constexpr (E == 2)
+      return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, kCached);
+    else
+      return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kCached);
+  };
+  auto widen = [](uint32_t u) -> float { return __builtin_bit_cast(float, E == 2 ? u << 16 : u); };
+  auto load_xd = [&]<bool FULL>(int64_t t_tile, uint32_t (&xr)[K], uint32_t (&dr)[K]) {
     const int64_t left = len - t_tile - j * K;
 #pragma unroll
     for (int i = 0; i < K; ++i) {
       const bool ok = FULL || i < left;
       const uint32_t sx = static_cast<uint32_t>((t_tile + i) * xd_step);
-      xv[i] = ok ? Elem<IO>::template load<kCached>(rx, off_xd, sx) : 0.0f;
-      dv[i] = ok ? Elem<IO>::template load<kCached>(rd, off_xd, sx) : 0.0f;
+      xr[i] = ok ? load_raw(rx, off_xd, sx) : 0u;
+      dr[i] = ok ? load_raw(rd, off_xd, sx) : 0u;
     }
   };
 
@@ -272,9 +281,15 @@ __global__ __launch_bounds__(64 * W, FOLD ? kFoldWavesPerSimd : kMinWavesPerSimd
   // beyond len are the identity and y there is +0.  When `prefetch` is set,
   // the next tile's x and delta are requested into nxv/ndv before the work
   // of this tile starts, so their latency hides behind it.
-  auto tile_body = [&]<bool FULL>(int64_t t_tile, int buf, float (&xv)[K], float (&dv)[K], bool prefetch,
-                                  float (&nxv)[K], float (&ndv)[K]) {
+  auto tile_body = [&]<bool FULL>(int64_t t_tile, int buf, const uint32_t (&xr)[K], const uint32_t (&dr)[K],
+                                  bool prefetch, uint32_t (&nxv)[K], uint32_t (&ndv)[K]) {
     const int64_t left = len - t_tile - j * K;  // valid steps from this lane's first step
+    float xv[K], dv[K];
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      xv[i] = widen(xr[i]);
+      dv[i] = widen(dr[i]);
+    }
     float bv[K], cv[K];
 #pragma unroll
     for (int i = 0; i < K; ++i) {
@@ -440,7 +455,7 @@ __global__ __launch_bounds__(64 * W, FOLD ? kFoldWavesPerSimd : kMinWavesPerSimd
 
   __syncthreads();  // a2s is written
   const int64_t nfull = len / T;
-  float xa[K], da[K], xn[K], dn[K];
+  uint32_t xa[K], da[K], xn[K], dn[K];
   if (nfull > 0) load_xd.template operator()<true>(0, xa, da);
   for (int64_t tile = 0; tile < nfull; ++tile) {
     tile_body.template operator()<true>(tile * T, FOLD ? 0 : static_cast<int>(tile & 1), xa, da, tile + 1 < nfull,
