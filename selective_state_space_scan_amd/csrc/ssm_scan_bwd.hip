@@ -718,7 +718,23 @@ __global__ __launch_bounds__(256) void ssm_bwd_reduce_kernel(ReduceParams p) {
       }
       float sb = 0.0f, sc = 0.0f;
       if (t < len) {
-        for (int g = 0; g < p.n_cg; ++g) {
+        // eight groups' loads in flight at once; the additions stay in group
+        // order
+        int g = 0;
+        for (; g + 8 <= p.n_cg; g += 8) {
+          float vb[8], vc[8];
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            vb[k] = p.ws_dB[(g + k) * n_bc + i];
+            vc[k] = p.ws_dC[(g + k) * n_bc + i];
+          }
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            sb += vb[k];
+            sc += vc[k];
+          }
+        }
+        for (; g < p.n_cg; ++g) {
           sb += p.ws_dB[g * n_bc + i];
           sc += p.ws_dC[g * n_bc + i];
         }
