@@ -5,8 +5,9 @@ A step is one call of the fused forward (every step of the method: softplus,
 discretisation, the scan with its chunk carry, readout, final state) over one
 batch of seeded synthetic input already resident in HBM.  The default workload
 is the headline one: batch 8, L 4096, dim 1024, dstate 16, bf16 I/O with fp32
-arithmetic.  Three copies of the inputs are rotated so that the 256 MB
-Infinity Cache cannot serve x and delta from a previous step.
+arithmetic.  Four copies of the inputs (over 512 MB together, twice the
+256 MB Infinity Cache) are rotated so that x and delta of a step cannot be
+served from a previous step's cache contents.
 
 Prints one JSON line on stdout: throughput in state updates per second
 (batch * L * dim * dstate per step, valid steps only for padded batches), the
@@ -15,7 +16,7 @@ timed on this host on the same workload.
 
 ``--pass bwd`` measures the backward instead (gradients of every input for
 seeded output gradients, from the chunk states of one untimed forward), with
-its own roofline and the oracle's backward timed on a slice of the channels.
+its own roofline and the oracle's backward timed on the same workload.
 """
 from __future__ import annotations
 
@@ -156,7 +157,7 @@ def main() -> int:
     # (measured: 205 us average after 5 warm-up launches, 192 us after 200).
     ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", type=int, default=2, help="workload index (default: the headline one)")
-    ap.add_argument("--rotate", type=int, default=3, help="input copies rotated between steps")
+    ap.add_argument("--rotate", type=int, default=4, help="input copies rotated between steps")
     ap.add_argument("--time-parts", type=int, default=0,
                     help="forward time split: parts to cut the sequence into (default 0: the library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
