@@ -149,6 +149,64 @@ def cpu_baseline(inp, w, threads: int, min_seconds: float = 1.0) -> dict:
                       f"{threads} threads over (b, d) rows; fp64, gcc -O2)"}
 
 
+def measure_peaks(dev) -> dict:
+    """Peak rates of this GPU from the microbenchmarks in libssmpeaks.so
+    (median of 10 timed launches after 3 warm-ups, HIP events on the
+    launching stream): HBM read and copy bandwidth (GB/s, copy counting read
+    plus write), the plain fp32 FMA rate (TFLOP/s, 2 per FMA) and the
+    v_exp_f32 rate (T exp/s)."""
+    import ctypes
+
+    import torch
+
+    from selective_state_space_scan_amd import build as B
+    if not os.path.exists(B.PEAKS_LIB_PATH):
+        raise FileNotFoundError(f"{B.PEAKS_LIB_PATH} is not built (python -m selective_state_space_scan_amd.build)")
+    lib = ctypes.CDLL(B.PEAKS_LIB_PATH)
+    lib.ssm_peak_launch.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.ssm_peak_launch.restype = ctypes.c_int
+    stream = torch.cuda.current_stream(dev)
+    blocks = 4096
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    big = torch.ones((1 << 30) // 4, dtype=torch.float32, device=dev)  # 1 GiB
+    dst = torch.empty((1 << 29) // 4, dtype=torch.float32, device=dev)  # 512 MiB
+
+    def timed(which, a, b, n4, iters):
+        ms = []
+        for r in range(13):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            rc = lib.ssm_peak_launch(which, a, b, n4, out.data_ptr(), blocks, iters, stream.cuda_stream)
+            e1.record(stream)
+            if rc != 0:
+                raise RuntimeError(f"ssm_peak_launch({which}) failed: {rc}")
+            torch.cuda.synchronize()
+            if r >= 3:
+                ms.append(e0.elapsed_time(e1))
+        return float(np.median(ms))
+
+    t_read = timed(0, big.data_ptr(), None, big.numel() // 4, 0)
+    t_copy = timed(1, big.data_ptr(), dst.data_ptr(), dst.numel() // 4, 0)
+    fma_iters, exp_iters = 2048, 512
+    t_fma = timed(2, None, None, 0, fma_iters)
+    t_exp = timed(3, None, None, 0, exp_iters)
+    threads = blocks * 256
+    del big, dst
+    return {"hbm_read_gbps": round((1 << 30) / (t_read * 1e-3) / 1e9, 1),
+            "hbm_copy_gbps": round(2 * (1 << 29) / (t_copy * 1e-3) / 1e9, 1),
+            "fp32_fma_tflops": round(threads * fma_iters * 16 * 2 / (t_fma * 1e-3) / 1e12, 2),
+            "exp_t_per_s": round(threads * exp_iters * 8 / (t_exp * 1e-3) / 1e12, 2)}
+
+
+def add_measured_peak(roof: dict, peaks: dict) -> None:
+    """The roofline's binding bound against the measured peak as well: plain
+    FMA TFLOP/s for an ALU bound, HBM read GB/s for an HBM bound."""
+    pm = peaks["fp32_fma_tflops"] if roof["bound"] == "alu" else peaks["hbm_read_gbps"]
+    roof["peak_measured"] = pm
+    roof["frac_measured"] = round(roof["achieved"] / pm, 4)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -161,6 +219,8 @@ def main() -> int:
     ap.add_argument("--time-parts", type=int, default=0,
                     help="forward time split: parts to cut the sequence into (default 0: the library's choice)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the peak-rate microbenchmarks (roofline against the published peak only)")
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (default: min(16, cpus))")
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
                     help="measure the forward (default) or the backward")
@@ -268,6 +328,9 @@ def main() -> int:
     roof["algorithmic_tflop"] = flops / 1e12
     roof["traffic_unit"] = "bytes per launch"
 
+    peaks = None if args.no_peaks else measure_peaks(dev)
+    if peaks is not None:
+        add_measured_peak(roof, peaks)
     out = {
         "metric": METRIC,
         "value": updates / (ms_per_step * 1e-3),
@@ -287,6 +350,8 @@ def main() -> int:
                    "time_parts": parts},
         "roofline": roof,
     }
+    if peaks is not None:
+        out["measured_peaks"] = peaks
     if not args.no_cpu_baseline:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
         out["cpu_baseline"] = cpu_baseline(inp, w, threads)
@@ -386,6 +451,9 @@ def bench_bwd(args, w, inp) -> int:
                  "hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes": nbytes,
                  "algorithmic_tflop": flops / 1e12, "traffic_unit": "bytes per launch"})
     roof.update(kernel_percentiles(kern_ms))
+    peaks = None if args.no_peaks else measure_peaks(dev)
+    if peaks is not None:
+        add_measured_peak(roof, peaks)
     out = {
         "metric": "selective-scan backward state-updates/s (B·L·D·N) + HBM GB/s",
         "value": updates / (ms_per_step * 1e-3),
@@ -405,6 +473,8 @@ def bench_bwd(args, w, inp) -> int:
                    "input_copies_rotated": len(sets)},
         "roofline": roof,
     }
+    if peaks is not None:
+        out["measured_peaks"] = peaks
     if not args.no_cpu_baseline:
         threads = args.cpu_threads or min(16, os.cpu_count() or 1)
         out["cpu_baseline"] = cpu_baseline_bwd(inp, cot, w, threads)

@@ -1,7 +1,8 @@
 """Compiles the HIP library (``libssmscan.so``) for gfx950 in-tree.
 
-The build is a single hipcc invocation over the forward and backward sources;
-it always recompiles when called.
+The build is one hipcc invocation over the forward and backward sources, and
+one for the benchmark's peak-rate microbenchmarks (``libssmpeaks.so``); it
+always recompiles when called.
 Packed fp32 VALU instructions are disabled for every HIP source
 (``-target-feature -packed-fp32-ops``).
 """
@@ -17,6 +18,10 @@ REPO_DIR = os.path.dirname(PKG_DIR)
 SRCS = [os.path.join(PKG_DIR, "csrc", f) for f in ("ssm_scan.hip", "ssm_scan_bwd.hip")]
 INCLUDE_DIR = os.path.join(REPO_DIR, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libssmscan.so")
+# The peak-rate microbenchmarks the benchmark measures the roofline with: a
+# library of their own, not part of the scan.
+PEAKS_SRC = os.path.join(PKG_DIR, "csrc", "ssm_peaks.hip")
+PEAKS_LIB_PATH = os.path.join(PKG_DIR, "libssmpeaks.so")
 ARCH = "gfx950"
 
 
@@ -27,19 +32,19 @@ def hipcc() -> str:
     raise FileNotFoundError("hipcc not found (ROCm toolchain required to build the HIP library)")
 
 
-def compile_command(out: str = LIB_PATH) -> list[str]:
+def compile_command(out: str = LIB_PATH, srcs: list[str] | None = None) -> list[str]:
+    srcs = SRCS if srcs is None else srcs
     return [
         hipcc(), "-O3", "-std=c++20", f"--offload-arch={ARCH}",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-fPIC", "-shared", "-Wall", f"-I{INCLUDE_DIR}",
-        "-o", out, *[s for s in SRCS if os.path.exists(s)],
+        "-o", out, *[s for s in srcs if os.path.exists(s)],
     ]
 
 
-def build(verbose: bool = False) -> str:
-    """Compile ``libssmscan.so`` next to this file and return its path."""
-    tmp = LIB_PATH + f".tmp{os.getpid()}"
-    cmd = compile_command(tmp)
+def _compile(out: str, srcs: list[str], verbose: bool) -> str:
+    tmp = out + f".tmp{os.getpid()}"
+    cmd = compile_command(tmp, srcs)
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -52,8 +57,15 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
     if verbose and msgs.strip():
         print(msgs, file=sys.stderr)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile ``libssmscan.so`` (and the benchmark's ``libssmpeaks.so``) next
+    to this file and return the scan library's path."""
+    _compile(PEAKS_LIB_PATH, [PEAKS_SRC], verbose)
+    return _compile(LIB_PATH, SRCS, verbose)
 
 
 if __name__ == "__main__":
