@@ -231,3 +231,20 @@ def test_binding_rejects_cpu_tensors():
     x = torch.zeros(1, 8, 16)
     with pytest.raises(ValueError):
         ssm.selective_scan_fwd(x, x, torch.zeros(16, 16), torch.zeros(1, 8, 16), torch.zeros(1, 8, 16))
+
+
+def test_peaks_library_loads_and_checks_arguments():
+    """The benchmark's peak-rate microbenchmark library is built beside the
+    scan library and rejects bad arguments before touching the GPU."""
+    from selective_state_space_scan_amd import build as B
+    assert os.path.exists(B.PEAKS_LIB_PATH), "run __graft_entry__.build() first"
+    lib = ctypes.CDLL(B.PEAKS_LIB_PATH)
+    f = lib.ssm_peak_launch
+    f.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                  ctypes.c_int, ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    assert f(2, None, None, 0, None, 0, 1, None) == -1     # no blocks
+    assert f(2, None, None, 0, None, 16, -1, None) == -1   # negative iterations
+    assert f(0, None, None, 16, None, 16, 0, None) == -1   # read without buffers
+    assert f(1, 8, None, 16, None, 16, 0, None) == -1      # copy without destination
+    assert f(7, None, None, 0, 8, 16, 0, None) == -1       # unknown benchmark
