@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 from conftest import rel_err
-from gpu_util import to_device, to_np64
+from gpu_util import to_device, to_np64, tol_for
 from selective_state_space_scan_amd import inputs as I
 
 pytestmark = pytest.mark.gpu
@@ -244,3 +244,37 @@ def test_bwd_outputs_only_4_byte_aligned():
         a = got.contiguous().view(bits).reshape(-1).cpu().numpy()
         b = ref[k].contiguous().view(bits).reshape(-1).cpu().numpy()
         assert np.array_equal(a, b), k
+
+
+@pytest.mark.parametrize("cfg", [1, 3, 4])
+def test_bwd_full_size_sampled_channels(cfg):
+    """The other full-size workloads (the variable-length batch, the long
+    dstate-64 sequence with the clip, which the library time-splits) in the
+    benchmark's launch configuration; the per-channel gradients (dx, ddelta,
+    dA_log, dD, dh0) of sampled 16-channel slices against the oracle's backward
+    run on those channels alone.  dB and dC sum over every channel and are
+    covered at full size by the headline test."""
+    import oracle
+    import torch
+    import selective_state_space_scan_amd as ssm
+    w = I.WORKLOADS[cfg]
+    inp = I.make_inputs(w, I.seed_for(cfg))
+    cot = I.make_cotangents(w, I.seed_for(cfg) + 500)
+    dev = to_device(inp, w.io)
+    y, h, cs = ssm.selective_scan_fwd(dev["x"], dev["delta"], dev["A_log"], dev["B"], dev["C"], dev["D"],
+                                      dev["valid_len"], delta_clamp=w.delta_clamp, return_chunk_states=True,
+                                      chunk_len=ssm.bwd_chunk_len(w.dstate))
+    dy = torch.from_numpy(cot["dy"]).cuda().to(dev["x"].dtype)
+    g = ssm.selective_scan_bwd(dev["x"], dev["delta"], dev["A_log"], dev["B"], dev["C"], dev["D"], dev["valid_len"],
+                               dy, cs, dh_last=torch.from_numpy(cot["dh_last"]).cuda(), delta_clamp=w.delta_clamp)
+    torch.cuda.synchronize()
+    for c0 in (0, w.dim - 16):
+        sl = slice(c0, c0 + 16)
+        r = oracle.selective_scan_bwd(inp["x"][:, :, sl], inp["delta"][:, :, sl], inp["A_log"][sl], inp["B"],
+                                      inp["C"], inp["D"][sl], cot["dy"][:, :, sl], valid_len=inp["valid_len"],
+                                      dh_last=cot["dh_last"][:, sl], delta_clamp=w.delta_clamp, nthreads=16)
+        got = {"dx": g["dx"][:, :, sl], "ddelta": g["ddelta"][:, :, sl], "dA_log": g["dA_log"][sl],
+               "dD": g["dD"][sl], "dh0": g["dh0"][:, sl]}
+        worst = {k: rel_err(to_np64(v), r[k]) for k, v in got.items()}
+        print(w.name, c0, " ".join(f"{k} {v:.1e}" for k, v in worst.items()), flush=True)
+        assert all(v <= tol_for(w.io) for v in worst.values()), worst
