@@ -632,7 +632,7 @@ namespace {
 
 // Parts for an automatic time split: none while the (row, channel group)
 // workgroups alone fill the GPU; otherwise enough parts that the fold of the
-// first P-1 parts and the parts themselves each occupy every CU, at most 8
+// first P-1 parts and the parts themselves each occupy every CU, at most 16
 // and at least four tiles per part.
 int64_t auto_parts(const ssm_scan_handle_s* h, int64_t nb, int64_t L, int64_t nd, int64_t N) {
   if (N != 16 && N != 32 && N != 64) return 1;
