@@ -76,6 +76,35 @@ def test_bad_dims(kw, code):
     assert call(_dims(**kw)) == code
 
 
+TB = 1 << 40
+# Fake addresses 1 TiB apart, so that rows of up to 2 GiB never overlap.
+FAR = dict(x=1 * TB, delta=2 * TB, A_log=3 * TB, B=4 * TB, C=5 * TB, D=None, valid_len=None, y=6 * TB,
+           h_last=7 * TB)
+
+
+@pytest.mark.parametrize("io,esz,dim,dstate", [(ssm.SSM_IO_BF16, 2, 1024, 16), (ssm.SSM_IO_F32, 4, 1024, 16),
+                                               (ssm.SSM_IO_BF16, 2, 16, 64)])
+def test_row_size_limit(io, esz, dim, dstate):
+    """A batch row of x, delta, y (or of B, C when dstate > dim) must span fewer
+    than 2^31 bytes: the longest such sequence passes every argument check (and
+    meets the NULL handle), one step more is unsupported -- forward and
+    backward."""
+    longest = (2**31 - 1) // (max(dim, dstate) * esz)
+    ok = _dims(batch=1, seqlen=longest, dim=dim, dstate=dstate, io=io)
+    over = _dims(batch=1, seqlen=longest + 1, dim=dim, dstate=dstate, io=io)
+    assert call(ok, **FAR) == ssm.SSM_ERR_INVALID_ARG  # the handle
+    assert call(over, **FAR) == ssm.SSM_ERR_UNSUPPORTED
+    bio = ssm.ssm_scan_bwd_io(dy=8 * TB, chunk_states=9 * TB, dx=10 * TB, ddelta=11 * TB, dA_log=12 * TB,
+                              dB=13 * TB, dC=14 * TB, workspace=16 * TB, workspace_bytes=1 << 62)
+
+    def bwd(d):
+        return ssm.ssm_selective_scan_bwd(None, FAR["x"], FAR["delta"], FAR["A_log"], FAR["B"], FAR["C"], None,
+                                          None, d, None, bio, None)
+
+    assert bwd(ok) == ssm.SSM_ERR_INVALID_ARG  # the handle
+    assert bwd(over) == ssm.SSM_ERR_UNSUPPORTED
+
+
 def test_null_dims():
     lib = ssm.lib()
     assert lib.ssm_selective_scan_fwd(None, 1, 2, 3, 4, 5, None, None, 6, None, None, None) == ssm.SSM_ERR_INVALID_ARG

@@ -1,0 +1,113 @@
+"""The longest rows the library accepts: one batch row of x, delta and y (bf16,
+1024 channels) just under 2 GiB, the most that the kernels' 32-bit buffer
+offsets address (one step more is rejected on the host, see
+test_abi_host.py).  Forward (with the library's own time split and without
+one) and backward, checked on sampled channels against the oracle run on those
+channels alone; dB and dC sum over every channel and are left to the
+full-workload tests.
+
+x, delta and dy repeat with a period of P steps (P prime and unrelated to every
+tile length, so a step read from the wrong place gets other values), which
+keeps the host-side generation small; B and C are drawn whole."""
+import numpy as np
+import pytest
+
+from conftest import rel_err
+from gpu_util import to_np64, tol_for
+from selective_state_space_scan_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+ND, N = 1024, 16
+L = (2**31 - 1) // (ND * 2)  # 1048575 steps: rows of 2 GiB - 2 KiB
+P = 4099
+REPS = -(-L // P)
+
+
+def _recipe(seed=2024):
+    """The workloads' recipe (x ~ N(0,1), delta_raw = 0.5 N(0,1) - 4, B, C, D ~
+    N(0,1), A_log[d, n] = log(n + 1), bf16-exact), with periodic x, delta, dy."""
+    rng = np.random.default_rng(seed)
+    bf = I.round_to_bf16
+    return {
+        "x": bf(rng.standard_normal((P, ND), dtype=np.float32)),
+        "delta": bf(0.5 * rng.standard_normal((P, ND), dtype=np.float32) - 4.0),
+        "dy": bf(rng.standard_normal((P, ND), dtype=np.float32)),
+        "B": bf(rng.standard_normal((1, L, N), dtype=np.float32)),
+        "C": bf(rng.standard_normal((1, L, N), dtype=np.float32)),
+        "A_log": np.ascontiguousarray(np.broadcast_to(np.log(np.arange(1, N + 1, dtype=np.float32)), (ND, N))),
+        "D": rng.standard_normal(ND, dtype=np.float32),
+        "dh_last": rng.standard_normal((1, ND, N), dtype=np.float32),
+    }
+
+
+def _host(block, chans):
+    """[1, L, len(chans)] fp32: the periodic tensor's listed channels."""
+    return np.tile(block[:, chans], (REPS, 1))[:L][None]
+
+
+def _device(block):
+    """[1, L, ND] bf16 on the GPU (the first L steps of the repeated block)."""
+    import torch
+    t = torch.from_numpy(block).cuda().to(torch.bfloat16)
+    out = t.repeat(REPS, 1)[:L].unsqueeze(0)
+    assert out.is_contiguous() and out.shape == (1, L, ND)
+    return out
+
+
+def _device_inputs(r):
+    import torch
+    return dict(x=_device(r["x"]), delta=_device(r["delta"]),
+                B=torch.from_numpy(r["B"]).cuda().to(torch.bfloat16),
+                C=torch.from_numpy(r["C"]).cuda().to(torch.bfloat16),
+                A_log=torch.from_numpy(r["A_log"]).cuda(), D=torch.from_numpy(r["D"]).cuda())
+
+
+@pytest.mark.parametrize("time_parts", [None, 1])
+def test_forward_row_at_the_limit(time_parts):
+    import torch
+    import oracle
+    import selective_state_space_scan_amd as ssm
+    r = _recipe()
+    dv = _device_inputs(r)
+    print(f"forward, L {L}, time_parts {time_parts}", flush=True)
+    y, h = ssm.selective_scan_fwd(dv["x"], dv["delta"], dv["A_log"], dv["B"], dv["C"], dv["D"], None,
+                                  time_parts=time_parts)
+    torch.cuda.synchronize()
+    chans = [0, 1, 15, 16, 511, 1007, 1008, 1023]
+    yr, hr = oracle.selective_scan(_host(r["x"], chans), _host(r["delta"], chans), r["A_log"][chans], r["B"],
+                                   r["C"], r["D"][chans], nthreads=8)
+    yg = np.stack([to_np64(y[0, :, d]) for d in chans], axis=1)[None]
+    hg = np.stack([to_np64(h[0, d]) for d in chans])[None]
+    ey, eh = rel_err(yg, yr), rel_err(hg, hr)
+    # the last steps carry the largest offsets: compare them on their own too
+    et = rel_err(yg[:, -300:], yr[:, -300:])
+    print(f"y {ey:.2e} (last 300 steps {et:.2e}), h_last {eh:.2e}", flush=True)
+    assert ey <= tol_for("bf16") and et <= tol_for("bf16") and eh <= tol_for("bf16")
+
+
+def test_backward_row_at_the_limit():
+    import torch
+    import oracle
+    import selective_state_space_scan_amd as ssm
+    r = _recipe()
+    dv = _device_inputs(r)
+    print(f"backward, L {L}", flush=True)
+    y, h, cs = ssm.selective_scan_fwd(dv["x"], dv["delta"], dv["A_log"], dv["B"], dv["C"], dv["D"], None,
+                                      return_chunk_states=True, chunk_len=ssm.bwd_chunk_len(N))
+    del y
+    dy = _device(r["dy"])
+    g = ssm.selective_scan_bwd(dv["x"], dv["delta"], dv["A_log"], dv["B"], dv["C"], dv["D"], None, dy, cs,
+                               dh_last=torch.from_numpy(r["dh_last"]).cuda())
+    torch.cuda.synchronize()
+    # the last channel group: the largest per-lane offsets
+    chans = list(range(ND - 16, ND))
+    ref = oracle.selective_scan_bwd(_host(r["x"], chans), _host(r["delta"], chans), r["A_log"][chans], r["B"],
+                                    r["C"], r["D"][chans], _host(r["dy"], chans), dh_last=r["dh_last"][:, chans],
+                                    nthreads=16)
+    sl = slice(ND - 16, ND)
+    got = {"dx": g["dx"][:, :, sl], "ddelta": g["ddelta"][:, :, sl], "dA_log": g["dA_log"][sl], "dD": g["dD"][sl],
+           "dh0": g["dh0"][:, sl]}
+    worst = {k: rel_err(to_np64(v), ref[k]) for k, v in got.items()}
+    print(" ".join(f"{k} {v:.1e}" for k, v in worst.items()), flush=True)
+    assert all(v <= tol_for("bf16") for v in worst.values()), worst
