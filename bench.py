@@ -201,10 +201,14 @@ def measure_peaks(dev) -> dict:
 
 def add_measured_peak(roof: dict, peaks: dict) -> None:
     """The roofline's binding bound against the measured peak as well: plain
-    FMA TFLOP/s for an ALU bound, HBM read GB/s for an HBM bound."""
+    FMA TFLOP/s for an ALU bound, HBM read GB/s for an HBM bound; and the
+    algorithmic HBM rate against the measured copy rate (read + write bytes,
+    like the algorithmic count)."""
     pm = peaks["fp32_fma_tflops"] if roof["bound"] == "alu" else peaks["hbm_read_gbps"]
     roof["peak_measured"] = pm
     roof["frac_measured"] = round(roof["achieved"] / pm, 4)
+    if "hbm_gbps" in roof and peaks.get("hbm_copy_gbps"):
+        roof["hbm_frac_measured_copy"] = round(roof["hbm_gbps"] / peaks["hbm_copy_gbps"], 4)
 
 
 def main() -> int:

@@ -62,6 +62,10 @@ def test_measured_peak_fraction():
     roof = {"bound": "hbm", "achieved": 3000.0}
     bench.add_measured_peak(roof, {"fp32_fma_tflops": 125.0, "hbm_read_gbps": 6000.0})
     assert roof["peak_measured"] == 6000.0 and roof["frac_measured"] == 0.5
+    assert "hbm_frac_measured_copy" not in roof  # no copy rate measured
+    roof = {"bound": "alu", "achieved": 50.0, "hbm_gbps": 1000.0}
+    bench.add_measured_peak(roof, {"fp32_fma_tflops": 125.0, "hbm_read_gbps": 6000.0, "hbm_copy_gbps": 4000.0})
+    assert roof["hbm_frac_measured_copy"] == 0.25
 
 
 def test_traffic_record_needs_matching_sources(tmp_path, monkeypatch):
