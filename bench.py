@@ -128,6 +128,21 @@ def kernel_percentiles(kern_ms) -> dict:
             "kernel_ms_p90": round(float(p[2]), 5)}
 
 
+def host_cpu() -> dict:
+    """The host the CPU baseline ran on: processor model, logical CPUs, and
+    the CPUs this process may use."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(), "usable_cpus": len(os.sched_getaffinity(0))}
+
+
 def cpu_baseline(inp, w, threads: int, min_seconds: float = 1.0) -> dict:
     """The fp64 oracle on the host, over the whole workload, repeated until at
     least `min_seconds` of wall time (so `threads` x that of CPU work)."""
@@ -146,7 +161,7 @@ def cpu_baseline(inp, w, threads: int, min_seconds: float = 1.0) -> dict:
     upd = steps * w.dim * w.dstate * passes
     return {"value": upd / dt, "unit": "state-updates/s", "cores": threads, "kind": "oracle",
             "sample": f"the whole {w.name} workload, {passes} passes ({upd} state updates, {dt:.2f} s wall, "
-                      f"{threads} threads over (b, d) rows; fp64, gcc -O2)"}
+                      f"{threads} threads over (b, d) rows; fp64, gcc -O2)", "host": host_cpu()}
 
 
 def measure_peaks(dev) -> dict:
@@ -383,7 +398,7 @@ def cpu_baseline_bwd(inp, cot, w, threads: int, min_seconds: float = 2.0) -> dic
     used = min(threads, w.batch)  # the oracle's backward deals batch rows to threads
     return {"value": upd / dt, "unit": "state-updates/s", "cores": used, "kind": "oracle",
             "sample": f"the whole {w.name} workload, {passes} passes ({upd} state updates, {dt:.2f} s wall, "
-                      f"{used} threads over batch rows; fp64, gcc -O2)"}
+                      f"{used} threads over batch rows; fp64, gcc -O2)", "host": host_cpu()}
 
 
 def bench_bwd(args, w, inp) -> int:

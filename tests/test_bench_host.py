@@ -94,3 +94,9 @@ def test_committed_records_parse():
             pytest.skip(f"no {kind} record")
         keys = {l.split(":", 1)[0].strip() for l in open(path) if ":" in l and not l.startswith("#")}
         assert {"kernel_source_sha256", "hbm_bytes_per_launch"} <= keys
+
+
+def test_host_cpu_description():
+    h = bench.host_cpu()
+    assert set(h) == {"cpu_model", "nproc", "usable_cpus"}
+    assert isinstance(h["cpu_model"], str) and h["nproc"] >= 1 and 1 <= h["usable_cpus"] <= h["nproc"]
