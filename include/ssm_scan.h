@@ -65,7 +65,8 @@ enum ssm_status {
   SSM_OK = 0,
   SSM_ERR_INVALID_ARG = -1,     /* NULL required pointer or handle, negative dim, bad flag or clip bounds */
   SSM_ERR_UNSUPPORTED = -2,     /* dstate not 16/32/64, dim not a multiple of 16, misaligned pointer, wrong GPU,
-                                   one batch row of x, delta, B or C over 2 GiB, or a grid too large */
+                                   one batch row of x, delta, B or C spanning 2 GiB or more, or a grid too
+                                   large */
   SSM_ERR_ALIAS = -3,           /* y or h_last overlaps an input, or y overlaps h_last */
   SSM_ERR_HIP = -4,             /* a HIP runtime or launch error */
   SSM_ERR_NO_DEVICE = -5,       /* no usable GPU at the requested ordinal */
@@ -236,7 +237,9 @@ int64_t ssm_scan_bwd_chunk_len(int64_t dstate);
  * fill the GPU); -1 for NULL or invalid dims. */
 int64_t ssm_scan_bwd_workspace_bytes(const ssm_scan_dims* dims);
 
-/* Enqueue the backward on `stream` (two kernels).  Same conventions as the
+/* Enqueue the backward on `stream` (the main kernel and the reduction of the
+ * partial sums; with a time split a fold kernel first; for seqlen == 0 only
+ * small fill kernels).  Same conventions as the
  * forward: host-side checks first (SSM_ERR_INVALID_ARG also for a missing
  * required output, chunk_states or workspace, or a workspace that is too
  * small), nothing enqueued on failure, bitwise reproducible results. */
