@@ -277,3 +277,17 @@ def test_peaks_library_loads_and_checks_arguments():
     assert f(0, None, None, 16, None, 16, 0, None) == -1   # read without buffers
     assert f(1, 8, None, 16, None, 16, 0, None) == -1      # copy without destination
     assert f(7, None, None, 0, 8, 16, 0, None) == -1       # unknown benchmark
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the HIP library every entry point raises: there is no other
+    path to fall back to."""
+    from selective_state_space_scan_amd import _binding as B
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "libssmscan.so"))
+    with pytest.raises(ImportError, match="HIP library not built"):
+        B.lib()
+    for call_ in (lambda: B.chunk_len(16), lambda: B.bwd_chunk_len(16), lambda: B.error_string(0),
+                  lambda: B.ssm_scan_create(0)):
+        with pytest.raises(ImportError):
+            call_()
