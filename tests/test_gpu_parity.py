@@ -100,7 +100,7 @@ def test_closed_form_through_abi(io):
 @pytest.mark.parametrize("L", [1, 2, 3, 7, 8, 9, 31, 33, 64, 65, 127, 128, 129, 200])
 def test_fp32_short_lengths(L):
     """pwwt.cn section 4.4: short lengths (8 to 64 and around) against the serial
-    reference, fp32 I/O; expect max abs error around 1e-5 or better."""
+    fp64 oracle, fp32 I/O; expect max abs error around 1e-5 or better."""
     w = I.small_workload(I.WORKLOADS[0], batch=2, seqlen=L, dim=32)
     ey, eh = _check_full(w, I.make_inputs(w, 77 + L))
     assert ey <= 1e-4
