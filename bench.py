@@ -57,10 +57,12 @@ FLOPEQ_BWD_PER_UPDATE = 32.0
 FLOPEQ_BWD_PER_ROW_STEP = 54.0
 
 PROFILES = os.path.join(HERE, "profiles")
-# Each pass's kernel sources: a traffic record applies only to the build it was taken on.
+# Each pass's kernel sources and the build script that holds their compiler
+# flags: a traffic record applies only to the build it was taken on.
 _CSRC = os.path.join(HERE, "selective_state_space_scan_amd", "csrc")
-KERNEL_SRCS = [os.path.join(_CSRC, f) for f in ("ssm_scan.hip", "ssm_internal.h")]
-BWD_KERNEL_SRCS = [os.path.join(_CSRC, f) for f in ("ssm_scan_bwd.hip", "ssm_internal.h")]
+_BUILD = os.path.join(HERE, "selective_state_space_scan_amd", "build.py")
+KERNEL_SRCS = [os.path.join(_CSRC, f) for f in ("ssm_scan.hip", "ssm_internal.h")] + [_BUILD]
+BWD_KERNEL_SRCS = [os.path.join(_CSRC, f) for f in ("ssm_scan_bwd.hip", "ssm_internal.h")] + [_BUILD]
 TRAFFIC_RECORDS = {"fwd": ("ssm_fwd_kernel", KERNEL_SRCS), "bwd": ("ssm_bwd_kernel", BWD_KERNEL_SRCS)}
 
 

@@ -1,17 +1,19 @@
 """Compiles the HIP library (``libssmscan.so``) for gfx950 in-tree.
 
-The build is one hipcc invocation over the forward and backward sources, and
-one for the benchmark's peak-rate microbenchmarks (``libssmpeaks.so``); it
-always recompiles when called.
+Each source is compiled to an object with its own flags and the objects are
+linked into one shared library; the benchmark's peak-rate microbenchmarks
+(``libssmpeaks.so``) are a second library.  Every call recompiles.
 Packed fp32 VALU instructions are disabled for every HIP source
 (``-target-feature -packed-fp32-ops``).
 """
 from __future__ import annotations
 
+import concurrent.futures
 import os
 import shutil
 import subprocess
 import sys
+import tempfile
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 REPO_DIR = os.path.dirname(PKG_DIR)
@@ -32,19 +34,27 @@ def hipcc() -> str:
     raise FileNotFoundError("hipcc not found (ROCm toolchain required to build the HIP library)")
 
 
-def compile_command(out: str = LIB_PATH, srcs: list[str] | None = None) -> list[str]:
-    srcs = SRCS if srcs is None else srcs
-    return [
-        hipcc(), "-O3", "-std=c++20", f"--offload-arch={ARCH}",
-        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-fPIC", "-shared", "-Wall", f"-I{INCLUDE_DIR}",
-        "-o", out, *[s for s in srcs if os.path.exists(s)],
-    ]
+# Flags of one source beyond the common ones.  The forward is scheduled with
+# the AMDGPU backend's memory-clause strategy, which keeps a tile's loads
+# together: 1-4 % faster on every forward workload (same-GPU comparison);
+# the backward keeps the default, which was 0.7 % faster for it.
+SRC_FLAGS = {"ssm_scan.hip": ["-mllvm", "-amdgpu-sched-strategy=max-memory-clause"]}
 
 
-def _compile(out: str, srcs: list[str], verbose: bool) -> str:
-    tmp = out + f".tmp{os.getpid()}"
-    cmd = compile_command(tmp, srcs)
+def _common() -> list[str]:
+    return [hipcc(), "-O3", "-std=c++20", f"--offload-arch={ARCH}",
+            "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-fPIC", "-Wall", f"-I{INCLUDE_DIR}"]
+
+
+def object_command(obj: str, src: str) -> list[str]:
+    return [*_common(), *SRC_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
+
+
+def link_command(out: str, objs: list[str]) -> list[str]:
+    return [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", out, *objs]
+
+
+def _run(cmd: list[str], verbose: bool) -> None:
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -52,11 +62,27 @@ def _compile(out: str, srcs: list[str], verbose: bool) -> str:
     noise = "is not a recognized feature for this target"
     msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)
     if res.returncode != 0:
-        if os.path.exists(tmp):
-            os.remove(tmp)
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
     if verbose and msgs.strip():
         print(msgs, file=sys.stderr)
+
+
+def _compile(out: str, srcs: list[str], verbose: bool) -> str:
+    """Objects of `srcs`, linked into the shared library `out` (replaced only
+    once the link succeeded)."""
+    tmp = out + f".tmp{os.getpid()}"
+    with tempfile.TemporaryDirectory(prefix="ssmbuild") as d:
+        objs = [os.path.join(d, os.path.splitext(os.path.basename(src))[0] + ".o") for src in srcs]
+        # one hipcc per source, side by side
+        with concurrent.futures.ThreadPoolExecutor(max_workers=len(srcs)) as pool:
+            for f in [pool.submit(_run, object_command(o, src), verbose) for o, src in zip(objs, srcs)]:
+                f.result()
+        try:
+            _run(link_command(tmp, objs), verbose)
+        except RuntimeError:
+            if os.path.exists(tmp):
+                os.remove(tmp)
+            raise
     os.replace(tmp, out)
     return out
 
