@@ -71,6 +71,9 @@ def test_valid_arguments_reach_the_handle_check():
     (dict(dstate=8), ssm.SSM_ERR_UNSUPPORTED),
     (dict(dstate=17), ssm.SSM_ERR_UNSUPPORTED),
     (dict(dim=24), ssm.SSM_ERR_UNSUPPORTED),
+    # grid limits: one workgroup per (row, 16 channels), fewer than 2^31 of them
+    (dict(batch=2**31, dim=16), ssm.SSM_ERR_UNSUPPORTED),
+    (dict(batch=2**20, dim=2**16), ssm.SSM_ERR_UNSUPPORTED),
 ])
 def test_bad_dims(kw, code):
     assert call(_dims(**kw)) == code
