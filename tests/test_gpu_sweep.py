@@ -14,7 +14,7 @@ from selective_state_space_scan_amd import inputs as I
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 48
+N_CASES = 160
 
 
 def _draw(case: int):
