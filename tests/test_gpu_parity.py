@@ -116,6 +116,8 @@ def test_fp32_error_trend_with_length():
         errs.append(max(ey, eh))
     print("error vs L:", errs)
     assert max(errs) <= 1e-4
+    # bounded growth over a 32x longer sequence (measured: flat, 4e-7 to 5e-7)
+    assert max(errs) <= 4 * min(errs) + 1e-7
 
 
 @pytest.mark.parametrize("N", [16, 32, 64])
