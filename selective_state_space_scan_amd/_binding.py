@@ -220,6 +220,20 @@ def handle_for(device_index: int) -> int:
         return h
 
 
+def _stream_for(stream, dev):
+    """The stream to enqueue on as a torch stream object: the current stream of
+    ``dev`` for None, a torch stream as given, and a raw hipStream_t handle
+    wrapped as an external stream.  The tensors a call allocates are allocated
+    with that stream current, so that the caching allocator orders their reuse
+    after the call's kernels."""
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream(dev)
+    if isinstance(stream, torch.cuda.Stream):
+        return stream
+    return torch.cuda.ExternalStream(int(stream), device=dev)
+
+
 def selective_scan_fwd(x, delta, A_log, B, C, D=None, valid_len=None, *, delta_softplus: bool = True,
                        delta_clamp=None, y=None, h_last=None, return_h_last: bool = True, h0=None, delta_bias=None,
                        z=None, return_chunk_states: bool = False, chunk_len=None, time_parts=None, workspace=None,
@@ -274,14 +288,11 @@ def selective_scan_fwd(x, delta, A_log, B, C, D=None, valid_len=None, *, delta_s
     if valid_len is not None and (tuple(valid_len.shape) != (nb,) or valid_len.dtype != torch.int32
                                   or valid_len.device != dev or not valid_len.is_contiguous()):
         raise ValueError("valid_len must be a contiguous [batch] int32 tensor on x's device")
-    if y is None:
-        y = torch.empty_like(x)
-    elif tuple(y.shape) != (nb, L, nd) or y.dtype != x.dtype or y.device != dev or not y.is_contiguous():
+    if y is not None and (tuple(y.shape) != (nb, L, nd) or y.dtype != x.dtype or y.device != dev
+                          or not y.is_contiguous()):
         raise ValueError("y must be a contiguous tensor like x")
-    if h_last is None and return_h_last:
-        h_last = torch.empty((nb, nd, N), dtype=torch.float32, device=dev)
-    elif h_last is not None and (tuple(h_last.shape) != (nb, nd, N) or h_last.dtype != torch.float32
-                                 or h_last.device != dev or not h_last.is_contiguous()):
+    if h_last is not None and (tuple(h_last.shape) != (nb, nd, N) or h_last.dtype != torch.float32
+                               or h_last.device != dev or not h_last.is_contiguous()):
         raise ValueError("h_last must be a contiguous [batch, dim, dstate] float32 tensor")
 
     for name, t, shape in (("h0", h0, (nb, nd, N)), ("delta_bias", delta_bias, (nd,))):
@@ -292,9 +303,18 @@ def selective_scan_fwd(x, delta, A_log, B, C, D=None, valid_len=None, *, delta_s
                           or not z.is_contiguous()):
         raise ValueError("z must be a contiguous tensor like x")
     cl = _default_chunk_len(N) if chunk_len is None else int(chunk_len)
+    if return_chunk_states and cl <= 0:
+        raise ValueError(f"no chunk length for dstate {N} (unsupported) or chunk_len <= 0")
+    stream = _stream_for(stream, dev)
+    sptr = stream.cuda_stream
     chunk_states = None
-    if return_chunk_states:
-        chunk_states = torch.empty((nb, (L + cl - 1) // cl, nd, N), dtype=torch.float32, device=dev)
+    with torch.cuda.stream(stream):
+        if y is None:
+            y = torch.empty_like(x)
+        if h_last is None and return_h_last:
+            h_last = torch.empty((nb, nd, N), dtype=torch.float32, device=dev)
+        if return_chunk_states:
+            chunk_states = torch.empty((nb, (L + cl - 1) // cl, nd, N), dtype=torch.float32, device=dev)
     dims = ssm_scan_dims()
     dims.batch, dims.seqlen, dims.dim, dims.dstate = nb, L, nd, N
     dims.io_dtype = io
@@ -302,9 +322,6 @@ def selective_scan_fwd(x, delta, A_log, B, C, D=None, valid_len=None, *, delta_s
     if delta_clamp is not None:
         dims.delta_clamp = 1
         dims.delta_min, dims.delta_max = float(delta_clamp[0]), float(delta_clamp[1])
-    if stream is None:
-        stream = torch.cuda.current_stream(dev)
-    sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
 
     def ptr(t):
         return None if t is None or t.numel() == 0 else t.data_ptr()
@@ -317,9 +334,8 @@ def selective_scan_fwd(x, delta, A_log, B, C, D=None, valid_len=None, *, delta_s
         ws_bytes = workspace_bytes(dims, parts) if parts >= 2 else 0
         if ws_bytes > 0:
             if workspace is None:
-                workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-                if hasattr(stream, "cuda_stream"):
-                    workspace.record_stream(stream)  # freed only after the stream's work
+                with torch.cuda.stream(stream):
+                    workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
             elif (workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous()
                   or workspace.numel() < ws_bytes):
                 raise ValueError(f"workspace must be a contiguous uint8 tensor of at least {ws_bytes} bytes on {dev}")
@@ -390,13 +406,17 @@ def selective_scan_bwd(x, delta, A_log, B, C, D, valid_len, dy, chunk_states, *,
     if valid_len is not None and (tuple(valid_len.shape) != (nb,) or valid_len.dtype != torch.int32
                                   or valid_len.device != dev or not valid_len.is_contiguous()):
         raise ValueError("valid_len must be a contiguous [batch] int32 tensor on x's device")
-    out = dict(dx=torch.empty_like(x), ddelta=torch.empty_like(x), dz=torch.empty_like(x) if z is not None else None,
-               dA_log=torch.empty((nd, N), dtype=torch.float32, device=dev),
-               dB=torch.empty((nb, L, N), dtype=torch.float32, device=dev),
-               dC=torch.empty((nb, L, N), dtype=torch.float32, device=dev),
-               dD=torch.empty(nd, dtype=torch.float32, device=dev) if D is not None else None,
-               ddelta_bias=torch.empty(nd, dtype=torch.float32, device=dev) if delta_bias is not None else None,
-               dh0=torch.empty((nb, nd, N), dtype=torch.float32, device=dev))
+    stream = _stream_for(stream, dev)
+    sptr = stream.cuda_stream
+    with torch.cuda.stream(stream):
+        out = dict(dx=torch.empty_like(x), ddelta=torch.empty_like(x),
+                   dz=torch.empty_like(x) if z is not None else None,
+                   dA_log=torch.empty((nd, N), dtype=torch.float32, device=dev),
+                   dB=torch.empty((nb, L, N), dtype=torch.float32, device=dev),
+                   dC=torch.empty((nb, L, N), dtype=torch.float32, device=dev),
+                   dD=torch.empty(nd, dtype=torch.float32, device=dev) if D is not None else None,
+                   ddelta_bias=torch.empty(nd, dtype=torch.float32, device=dev) if delta_bias is not None else None,
+                   dh0=torch.empty((nb, nd, N), dtype=torch.float32, device=dev))
     dims = ssm_scan_dims()
     dims.batch, dims.seqlen, dims.dim, dims.dstate = nb, L, nd, N
     dims.io_dtype = io
@@ -404,9 +424,6 @@ def selective_scan_bwd(x, delta, A_log, B, C, D, valid_len, dy, chunk_states, *,
     if delta_clamp is not None:
         dims.delta_clamp = 1
         dims.delta_min, dims.delta_max = float(delta_clamp[0]), float(delta_clamp[1])
-    if stream is None:
-        stream = torch.cuda.current_stream(dev)
-    sptr = stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
 
     def ptr(t):
         return None if t is None or t.numel() == 0 else t.data_ptr()
@@ -415,9 +432,8 @@ def selective_scan_bwd(x, delta, A_log, B, C, D, valid_len, dy, chunk_states, *,
     if nbytes < 0:
         raise ValueError("unsupported dims for the backward")
     if workspace is None:
-        workspace = torch.empty(max(nbytes, 4), dtype=torch.uint8, device=dev)
-        if hasattr(stream, "cuda_stream"):
-            workspace.record_stream(stream)
+        with torch.cuda.stream(stream):
+            workspace = torch.empty(max(nbytes, 4), dtype=torch.uint8, device=dev)
     elif (workspace.dtype != torch.uint8 or workspace.device != dev or workspace.numel() < nbytes
           or not workspace.is_contiguous()):
         raise ValueError(f"workspace must be a contiguous uint8 tensor of at least {nbytes} bytes on {dev}")

@@ -126,6 +126,34 @@ def test_concurrent_streams():
         assert np.array_equal(_bits(b[0]), _bits(r2[0])) and np.array_equal(_bits(b[1]), _bits(r2[1]))
 
 
+def test_explicit_stream_argument():
+    """stream= given as a torch stream and as a raw hipStream_t handle (not the
+    current stream): the same bits as calls on the current stream, for a
+    forward that splits time (its scratch allocated by the binding) and for the
+    backward."""
+    import torch
+    import selective_state_space_scan_amd as ssm
+    w = I.small_workload(I.WORKLOADS[2], batch=2, seqlen=3000, dim=64)
+    d = to_device(I.make_inputs(w, 5), w.io)
+    cot = I.make_cotangents(w, 6)
+    dy = torch.from_numpy(cot["dy"]).cuda().to(d["x"].dtype)
+    args = (d["x"], d["delta"], d["A_log"], d["B"], d["C"], d["D"], None)
+    cl = ssm.bwd_chunk_len(w.dstate)
+    ref = [t.clone() for t in ssm.selective_scan_fwd(*args, time_parts=3, return_chunk_states=True, chunk_len=cl)]
+    gref = {k: v.clone() for k, v in ssm.selective_scan_bwd(*args, dy, ref[2]).items() if v is not None}
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    for st in (s, s.cuda_stream):
+        y, h, cs = ssm.selective_scan_fwd(*args, time_parts=3, return_chunk_states=True, chunk_len=cl, stream=st)
+        g = ssm.selective_scan_bwd(*args, dy, cs, stream=st)
+        s.synchronize()
+        for a, b in zip((y, h, cs), ref):
+            assert np.array_equal(_bits(a), _bits(b))
+        for k, v in gref.items():
+            assert np.array_equal(_bits(g[k]), _bits(v)), k
+
+
 def test_h_last_optional_and_outputs_given():
     import torch
     import selective_state_space_scan_amd as ssm
