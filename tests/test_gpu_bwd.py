@@ -179,6 +179,25 @@ def test_bwd_empty_and_degenerate():
     _compare(_gpu(inp, "f32"), _oracle(inp), 1e-4, "one group")
 
 
+def test_bwd_out_of_range_lengths_clamp():
+    """valid_len below 0 or above L acts as 0 or L (forward and backward),
+    bit for bit."""
+    L = 300
+    w, inp = _case("bf16", 16, L, 3, 32, seed=41, varlen=[-7, L + 55, 120])
+    w, ref = _case("bf16", 16, L, 3, 32, seed=41, varlen=[0, L, 120])
+    g, gr = _gpu(inp, "bf16"), _gpu(ref, "bf16")
+    for k, v in gr.items():
+        if v is not None:
+            a = g[k].contiguous().view(_int_view(g[k])).cpu().numpy()
+            b = v.contiguous().view(_int_view(v)).cpu().numpy()
+            assert np.array_equal(a, b), k
+
+
+def _int_view(t):
+    import torch
+    return torch.int16 if t.dtype == torch.bfloat16 else torch.int32
+
+
 def test_bwd_binding_rejects_bad_arguments():
     """The binding's own checks raise before anything is enqueued."""
     import torch
