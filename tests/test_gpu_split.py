@@ -115,3 +115,17 @@ def test_headline_shape_is_not_split():
     dims = ssm.ssm_scan_dims()
     dims.batch, dims.seqlen, dims.dim, dims.dstate, dims.io_dtype = w.batch, w.seqlen, w.dim, w.dstate, 1
     assert ssm.auto_time_parts(h, dims) == 16
+
+
+def test_auto_split_only_while_cus_would_idle():
+    """The library splits time only when the (row, 16-channel) groups would
+    leave CUs idle: at most two thirds as many groups as CUs."""
+    import selective_state_space_scan_amd as ssm
+    import torch
+    h = ssm._binding.handle_for(torch.cuda.current_device())
+    cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
+    for groups in (cus // 4, cus // 2, (2 * cus) // 3, (2 * cus) // 3 + 1, cus, (3 * cus) // 2, 2 * cus):
+        dims = ssm.ssm_scan_dims()
+        dims.batch, dims.seqlen, dims.dim, dims.dstate, dims.io_dtype = 1, 4096, 16 * groups, 16, 1
+        parts = ssm.auto_time_parts(h, dims)
+        assert (parts > 1) == (3 * groups <= 2 * cus), (groups, cus, parts)
