@@ -327,12 +327,13 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
   __syncthreads();  // a2s is written
 
   // The state entering tile kt (h0, or the chunk state the forward saved) is
-  // loaded at the top of the tile, so that its latency hides behind pass 1 --
-  // when a thread walks at most two pairs (dstate 16, 32); with four (dstate
-  // 64) the registers are not there, and it is loaded where the walk needs it.
-  // (Loading it a whole tile ahead costs a register copy at the loop's end,
-  // which waits for every outstanding memory operation, stores included.)
-  constexpr bool kAhead = PPL <= 2;
+  // loaded at the top of the tile, so that its latency hides behind pass 1.
+  // With four pairs per thread (dstate 64) that just fits in 256 VGPRs (the
+  // gated variants spill a few dwords) and is still 9 % faster than loading
+  // it where the walk needs it.  (Loading it a whole tile ahead costs a
+  // register copy at the loop's end, which waits for every outstanding memory
+  // operation, stores included.)
+  constexpr bool kAhead = PPL <= 4;
   auto load_h_in = [&](int64_t kt, int k) -> float {
     const int64_t gt = tile0 + kt;
     if (gt == 0) return (p.h0 != nullptr) ? p.h0[state_block + pair_offset(k)] : 0.0f;
