@@ -163,9 +163,10 @@ int64_t ssm_scan_chunk_len(int64_t dstate);
 
 /* The number of time parts the library picks for these dims on the handle's
  * GPU when time_parts = 0 (1 = no split): it splits only while the
- * (row, 16-channel) workgroups would leave CUs idle (at most two thirds as
- * many of them as CUs), into about four workgroups per resident slot.
- * Returns 1 for a NULL handle or dims, or invalid sizes. */
+ * (row, 16-channel) workgroups would leave CUs idle (at most three quarters
+ * as many of them as CUs), into about four workgroups per resident slot and
+ * parts of at least 512 steps.  Returns 1 for a NULL handle or dims, or
+ * invalid sizes. */
 int32_t ssm_scan_auto_time_parts(ssm_scan_t handle, const ssm_scan_dims* dims);
 
 /* Bytes of workspace a split into (at most) time_parts parts needs for these

@@ -641,16 +641,20 @@ int64_t auto_parts(const ssm_scan_handle_s* h, int64_t nb, int64_t L, int64_t nd
   // Split only while whole CUs would sit idle: a workgroup alone on a CU
   // runs about 1.6x faster than one that shares it, and the split adds the
   // fold (about half a forward's work) over all but one part.  Measured at
-  // 4096 steps, dstate 16, 256 CUs: 128 (row, 16-channel) groups 0.112 ms
-  // unsplit, 0.081 ms in 8 parts; 192 groups a tie; 256 groups 0.113 ms
-  // unsplit, 0.142 ms in 8 parts; 384 and 448 groups 10-26 % slower split.
-  if (groups <= 0 || 3 * groups > 2 * static_cast<int64_t>(h->cu_count)) return 1;
+  // 4096 steps on 256 CUs (ms, unsplit / best split): 128 (row, 16-channel)
+  // groups 0.112 / 0.081 (dstate 16), 0.250 / 0.158 (32), 0.527 / 0.318
+  // (64); 192 groups 0.113 / 0.113, 0.256 / 0.232, 0.529 / 0.457; 256 groups
+  // 0.113 / 0.135, 0.262 / 0.270, 0.539 / 0.548; more groups lose more.
+  if (groups <= 0 || 4 * groups > 3 * static_cast<int64_t>(h->cu_count)) return 1;
   // about four workgroups per slot (finer parts balance the tail better:
   // 2.43 ms at 8 parts, 2.34 ms at 16 for one row of 2048 channels x 32768
-  // steps, dstate 64), at most 16 parts
+  // steps, dstate 64), at most 16 parts, and parts of at least four tiles and
+  // 512 steps (shorter ones lose to the per-part prologue: 4096 steps, 128
+  // groups, dstate 32 and 64: 8 parts 6-8 % faster than 16)
   int64_t parts = (4 * slots + groups - 1) / groups;
   if (parts > 16) parts = 16;
-  const int64_t max_by_len = L / (4 * tile_steps(N));
+  const int64_t min_part = 4 * tile_steps(N) > 512 ? 4 * tile_steps(N) : 512;
+  const int64_t max_by_len = L / min_part;
   if (parts > max_by_len) parts = max_by_len;
   return parts < 1 ? 1 : split_for(L, N, parts).parts;
 }

@@ -92,7 +92,7 @@ def test_auto_split_small_batch_long_sequence():
     dims = ssm.ssm_scan_dims()
     dims.batch, dims.seqlen, dims.dim, dims.dstate, dims.io_dtype = 1, 4096, 64, 64, ssm.SSM_IO_BF16
     parts = ssm.auto_time_parts(ssm._binding.handle_for(torch.cuda.current_device()), dims)
-    assert parts == 16
+    assert parts == 4096 // 512  # as many as parts of at least 512 steps allow
     y, h, cs = _run(inp, "bf16", None, clamp=(1e-3, 0.1))
     yr, hr, csr = oracle.selective_scan(inp["x"], inp["delta"], inp["A_log"], inp["B"], inp["C"], inp["D"],
                                         delta_clamp=(1e-3, 0.1), chunk_len=ssm.chunk_len(64), nthreads=8)
@@ -119,13 +119,16 @@ def test_headline_shape_is_not_split():
 
 def test_auto_split_only_while_cus_would_idle():
     """The library splits time only when the (row, 16-channel) groups would
-    leave CUs idle: at most two thirds as many groups as CUs."""
+    leave CUs idle: at most three quarters as many groups as CUs; and parts
+    hold at least 512 steps."""
     import selective_state_space_scan_amd as ssm
     import torch
     h = ssm._binding.handle_for(torch.cuda.current_device())
     cus = torch.cuda.get_device_properties(torch.cuda.current_device()).multi_processor_count
-    for groups in (cus // 4, cus // 2, (2 * cus) // 3, (2 * cus) // 3 + 1, cus, (3 * cus) // 2, 2 * cus):
-        dims = ssm.ssm_scan_dims()
-        dims.batch, dims.seqlen, dims.dim, dims.dstate, dims.io_dtype = 1, 4096, 16 * groups, 16, 1
-        parts = ssm.auto_time_parts(h, dims)
-        assert (parts > 1) == (3 * groups <= 2 * cus), (groups, cus, parts)
+    for groups in (cus // 4, cus // 2, (3 * cus) // 4, (3 * cus) // 4 + 1, cus, (3 * cus) // 2, 2 * cus):
+        for N in (16, 32, 64):
+            dims = ssm.ssm_scan_dims()
+            dims.batch, dims.seqlen, dims.dim, dims.dstate, dims.io_dtype = 1, 4096, 16 * groups, N, 1
+            parts = ssm.auto_time_parts(h, dims)
+            assert (parts > 1) == (4 * groups <= 3 * cus), (groups, cus, N, parts)
+            assert parts <= 4096 // 512, (groups, N, parts)
