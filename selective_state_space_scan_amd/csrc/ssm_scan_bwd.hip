@@ -937,11 +937,11 @@ int ssm_selective_scan_bwd(ssm_scan_t handle, const void* x, const void* delta, 
   prm.dz = ex.z != nullptr ? io->dz : nullptr;
   prm.dh0 = io->dh0;
   // Time split: while the (row, channel group) grid would leave CUs idle (at
-  // most two thirds as many groups as CUs, the forward's rule), cut time into
-  // parts of whole tiles (at most 8, at least four tiles per part).  Above
-  // that the split costs more than it balances (measured at 4096 steps,
-  // dstate 16: 256 groups 0.369 ms split, 0.338 ms not; 448 groups 0.678 /
-  // 0.570 ms).
+  // most two thirds as many groups as CUs), cut time into parts of whole
+  // tiles (at most 8, at least four tiles per part).  Above that the split
+  // costs more than it balances (measured at 4096 steps: 192 groups 3 / 6 /
+  // 8 % slower split at dstate 16 / 32 / 64; dstate 16, 256 groups 0.369 ms
+  // split, 0.338 ms not; 448 groups 0.678 / 0.570 ms).
   const int64_t groups = nb * n_cg;
   const int64_t slots = 2 * static_cast<int64_t>(handle->cu_count);
   int64_t parts = 1, part_len = L;
