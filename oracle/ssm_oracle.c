@@ -215,7 +215,11 @@ static void* worker(void* argp) {
     int64_t ystride;
     if (j->rb) {
       b = j->rb[r];
+#if ORACLE_MUTATION == 14
+      d = j->rd[r > 0 ? r - 1 : 0];
+#else
       d = j->rd[r];
+#endif
       yo = j->y + r * p->L;
       ystride = 1;
       ho = j->h_last ? j->h_last + r * p->N : NULL;

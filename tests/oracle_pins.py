@@ -486,6 +486,37 @@ ALL_PINS = {
     "bwd_padding": pin_bwd_padding,
 }
 
+def pin_rows_match_full(orc, mutation=0):
+    """The row sampler the full-size GPU checks use: the forward restricted to
+    listed (b, d) rows equals the matching slices of the full forward bit for
+    bit (rows in any order, repeated, all rows of a batch), with padding
+    (lengths 0, partial and L), h0, delta bias, output gate and clip, on one
+    thread and on several -- every (b, d) row is the same serial loop, so the
+    two entry points may differ only in indexing."""
+    rng = np.random.default_rng(14)
+    nb, L, nd, N = 3, 37, 12, 4
+    x, delta, A_log, B, C, D = _rand_problem(rng, nb, L, nd, N)
+    vl = np.array([L, 11, 0], dtype=np.int32)
+    h0 = rng.standard_normal((nb, nd, N))
+    bias = 0.5 * rng.standard_normal(nd)
+    z = 2.0 * rng.standard_normal((nb, L, nd))
+    rows = [(1, 5), (0, 0), (2, 11), (1, 5), (0, 11)] + [(1, d) for d in range(nd)]
+    rows += [(int(rng.integers(nb)), int(rng.integers(nd))) for _ in range(9)]
+    rows = np.array(rows, dtype=np.int64)
+    for clamp in (None, (0.01, 0.02)):
+        y, h = orc.selective_scan(x, delta, A_log, B, C, D, valid_len=vl, h0=h0, delta_bias=bias, z=z,
+                                  delta_clamp=clamp, nthreads=2, mutation=mutation)
+        for nthreads in (1, 3):
+            yr, hr = orc.selective_scan_rows(x, delta, A_log, B, C, rows, D=D, valid_len=vl, h0=h0, delta_bias=bias,
+                                             z=z, delta_clamp=clamp, nthreads=nthreads, mutation=mutation)
+            assert yr.shape == (len(rows), L) and hr.shape == (len(rows), N)
+            for r, (bi, di) in enumerate(rows):
+                assert np.array_equal(yr[r], y[bi, :, di]), (clamp, nthreads, r, bi, di)
+                assert np.array_equal(hr[r], h[bi, di]), (clamp, nthreads, r, bi, di)
+
+
+ALL_PINS["rows_match_full"] = pin_rows_match_full
+
 # The planted mistakes (see ssm_oracle.c) and the pins expected to notice each.
 MUTATIONS = {
     1: ("input absorbed before the decay", {"closed_form_scan", "order_sensitivity", "bruteforce_scan"}),
@@ -501,4 +532,5 @@ MUTATIONS = {
     11: ("backward: adjoint not decayed through the step", {"bwd_finite_differences", "bwd_linearity"}),
     12: ("backward: dA without the delta factor", {"bwd_finite_differences"}),
     13: ("backward: softplus derivative missing", {"bwd_finite_differences"}),
+    14: ("row sampler pairs a row's b with the previous row's d", {"rows_match_full"}),
 }
