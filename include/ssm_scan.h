@@ -108,8 +108,9 @@ int ssm_selective_scan_fwd(ssm_scan_t handle, const void* x, const void* delta, 
  *               zeros (continuing a sequence processed in pieces: the split
  *               run equals the whole run, pwwt.cn section 4.2 and
  *               bjdmk.com.cn section 2.4 carry the state between chunks).
- *               h0 may be the same buffer as h_last (in-place update); any
- *               other overlap with an output is rejected.
+ *               h0 may be the same buffer as h_last (in-place update; the
+ *               scan then runs unsplit, whatever time_parts asks); any other
+ *               overlap with an output is rejected.
  *  delta_bias   [dim] fp32: added to delta before softplus and the clip (the
  *               dt bias of the fused kernel body in the nxbn.cn article,
  *               section 3).

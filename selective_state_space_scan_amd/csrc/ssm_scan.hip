@@ -789,8 +789,8 @@ int ssm_selective_scan_fwd_ex(ssm_scan_t handle, const void* x, const void* delt
                             D ? static_cast<size_t>(nd) * 4 : 0, valid_len ? static_cast<size_t>(nb) * 4 : 0,
                             ex.z ? n_xd * e : 0, ex.h0 ? n_state * 4 : 0, ex.delta_bias ? static_cast<size_t>(nd) * 4 : 0};
     for (int k = 0; k < 10; ++k) {
-      // h0 may be h_last itself: each state element is read before the same
-      // thread overwrites it.
+      // h0 may be h_last itself: unsplit, each state element is read before
+      // the same thread overwrites it (a split runs unsplit then, below).
       const bool h0_in_place = (ins[k] == ex.h0 && ex.h0 != nullptr && static_cast<const void*>(h_last) == ex.h0);
       if (overlaps(y, by, ins[k], ins_n[k]) || overlaps(ex.chunk_states, bcs, ins[k], ins_n[k]))
         return SSM_ERR_ALIAS;
@@ -860,6 +860,10 @@ int ssm_selective_scan_fwd_ex(ssm_scan_t handle, const void* x, const void* delt
     parts = auto_parts(handle, nb, L, nd, N);
     if (parts >= 2 && 4 * split_ws_floats(split_for(L, N, parts), nb, nd, N) > ex.workspace_bytes) parts = 1;
   }
+  // In place (h0 == h_last) the scan runs unsplit: split, the first part's
+  // workgroups would read h0 while the last part's, in the same launch, write
+  // h_last over it.
+  if (ex.h0 != nullptr && static_cast<const void*>(ex.h0) == static_cast<const void*>(h_last)) parts = 1;
   const Split sp = split_for(L, N, parts);
   if (static_cast<int64_t>(nb) * (nd / 16) * sp.parts > 0x7fffffffLL) return SSM_ERR_UNSUPPORTED;
   prm.ws = static_cast<float*>(ex.workspace);

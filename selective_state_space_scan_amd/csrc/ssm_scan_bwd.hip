@@ -32,8 +32,9 @@
 //    reverse walk from the adjoint carry leaves each sub-chunk's mu_{end+1};
 //  * pass 2: the lane rebuilds h over its K steps and runs the adjoint back
 //    over them, producing dx, dDelta_raw, dz, dA; the per-(step, state)
-//    contributions to dB and dC are summed over the 16 channels through LDS
-//    and written as one partial per channel group.
+//    contributions to dB and dC are summed over the 16 channels by a DPP
+//    reduce-scatter across the lanes and written as one partial per channel
+//    group.
 // A second kernel sums the partials over channel groups (dB, dC) and over
 // batch rows (dA_log, dD, dbias) in a fixed order, so the result is
 // deterministic.
@@ -886,7 +887,9 @@ int ssm_selective_scan_bwd(ssm_scan_t handle, const void* x, const void* delta, 
     for (const void* q : fs)
       if (!aligned(q, 4)) return SSM_ERR_UNSUPPORTED;
     const size_t bxd = L > 0 ? n_xd * e : 0;
-    const size_t bcs = static_cast<size_t>(n_tiles > 1 ? n_tiles - 1 : 0) * n_state * 4;
+    // chunk_states is read as [batch, n_tiles, dim, dstate] up to chunk
+    // n_tiles - 2 of the last row
+    const size_t bcs = n_tiles > 1 ? static_cast<size_t>(nb * n_tiles - 1) * nd * N * 4 : 0;
     const void* ins[] = {x, delta, B, C, A_log, D, valid_len, L > 0 ? ex.z : nullptr, ex.h0, ex.delta_bias,
                          L > 0 ? io->dy : nullptr, io->dh_last, io->chunk_states};
     const size_t ins_n[] = {n_xd * e, n_xd * e, n_bc * e, n_bc * e, static_cast<size_t>(nd) * N * 4,

@@ -236,6 +236,11 @@ def test_bwd_checks():
     assert call(io(dC=13 * MB + 64)) == ssm.SSM_ERR_ALIAS  # dB
     assert call(io(workspace=12 * MB)) == ssm.SSM_ERR_ALIAS  # dA_log
     assert call(io(dh0=9 * MB)) == ssm.SSM_ERR_ALIAS  # chunk states
+    # the chunk states read are [row, chunk] = [0..1, 0..3] up to (1, 2): 7 of the
+    # 8 [dim, dstate] blocks (2048 bytes each), the last row's included
+    assert call(io(dh0=9 * MB + 6 * 2048)) == ssm.SSM_ERR_ALIAS
+    assert call(io(dh0=9 * MB + 7 * 2048 - 4)) == ssm.SSM_ERR_ALIAS
+    assert call(io(dh0=9 * MB + 7 * 2048)) == ssm.SSM_ERR_INVALID_ARG  # past them: the NULL handle
     assert call(io(dD=11 * MB + 2)) == ssm.SSM_ERR_UNSUPPORTED  # misaligned
     assert ssm.ssm_selective_scan_bwd(None, *[None] * 7, d, None, io(), None) == ssm.SSM_ERR_INVALID_ARG
     assert ssm.ssm_selective_scan_bwd(None, *[None] * 7, _dims(dstate=8), None, io(), None) == \

@@ -6,7 +6,7 @@ import numpy as np
 import pytest
 
 from conftest import rel_err
-from gpu_util import to_device, to_np64, tol_for
+from gpu_util import oracle_bwd, to_device, to_np64, tol_for
 from selective_state_space_scan_amd import inputs as I
 
 pytestmark = pytest.mark.gpu
@@ -60,14 +60,16 @@ def _oracle(inp, clamp=None):
                                      delta_clamp=clamp, nthreads=8)
 
 
-def _compare(g, r, tol, label):
+def _compare(g, r, io, label):
+    """Every gradient against the oracle's, each to its own tolerance: bf16
+    outputs of bf16 I/O (dx, ddelta, dz) to 2e-2, every fp32 one to 1e-4."""
     worst = {}
     for k in GRADS:
         if r.get(k) is None or g.get(k) is None:
             continue
         worst[k] = rel_err(to_np64(g[k]), r[k])
     print(label, " ".join(f"{k} {v:.1e}" for k, v in worst.items()), flush=True)
-    bad = {k: v for k, v in worst.items() if not v <= tol}
+    bad = {k: v for k, v in worst.items() if not v <= tol_for(io, k)}
     assert not bad, bad
 
 
@@ -80,7 +82,7 @@ def test_bwd_against_oracle(io, N):
     w, inp = _case(io, N, L, 3, 32, seed=200 + N, varlen=[L, 3 * T + 5, 0])
     g = _gpu(inp, io)
     r = _oracle(inp)
-    _compare(g, r, 1e-4 if io == "f32" else 2e-2, f"{io} N={N}")
+    _compare(g, r, io, f"{io} N={N}")
     # padding: zero gradients past each row's length, the empty row's state adjoint passes through
     assert np.all(to_np64(g["dx"][1, 3 * T + 5:]) == 0) and np.all(to_np64(g["dB"][2]) == 0)
     assert np.array_equal(to_np64(g["dh0"][2]), inp["dh_last"][2].astype(np.float64))
@@ -91,12 +93,12 @@ def test_bwd_plain_and_clamped(io):
     """No extras (zero initial state, no bias, no gate), full rows; then the
     long-workload recipe's clip on delta."""
     w, inp = _case(io, 16, 300, 2, 48, seed=7, extras=False)
-    _compare(_gpu(inp, io), _oracle(inp), 1e-4 if io == "f32" else 2e-2, f"{io} plain")
+    _compare(_gpu(inp, io), _oracle(inp), io, f"{io} plain")
     w, inp = _case(io, 64, 200, 2, 32, seed=9, extras=False)
     shifted = (inp["delta"] - 1.0).astype(np.float32)  # softplus values on both sides of the clip
     inp["delta"] = I.round_to_bf16(shifted) if io == "bf16" else shifted
     clamp = (1e-3, 0.01)
-    _compare(_gpu(inp, io, clamp=clamp), _oracle(inp, clamp=clamp), 1e-4 if io == "f32" else 2e-2, f"{io} clamp")
+    _compare(_gpu(inp, io, clamp=clamp), _oracle(inp, clamp=clamp), io, f"{io} clamp")
 
 
 def test_bwd_short_and_single_tile():
@@ -104,7 +106,7 @@ def test_bwd_short_and_single_tile():
     import selective_state_space_scan_amd as ssm
     for L in (1, 5, ssm.bwd_chunk_len(16)):
         w, inp = _case("f32", 16, L, 2, 16, seed=L)
-        _compare(_gpu(inp, "f32"), _oracle(inp), 1e-4, f"L={L}")
+        _compare(_gpu(inp, "f32"), _oracle(inp), "f32", f"L={L}")
 
 
 def test_bwd_deterministic():
@@ -119,38 +121,47 @@ def test_bwd_deterministic():
 def test_bwd_after_time_split_forward():
     """The chunk states of a time-split forward serve the backward equally."""
     w, inp = _case("bf16", 64, 2048, 1, 32, seed=13)
-    _compare(_gpu(inp, "bf16", time_parts=4), _oracle(inp), 2e-2, "split fwd")
+    _compare(_gpu(inp, "bf16", time_parts=4), _oracle(inp), "bf16", "split fwd")
 
 
 def test_bwd_grid_filling_shape():
     """A grid of 512 (row, channel group) workgroups takes the four-wave
     kernel (smaller grids take the eight-wave one)."""
     w, inp = _case("bf16", 16, 200, 4, 2048, seed=17, varlen=[200, 77, 130, 5])
-    _compare(_gpu(inp, "bf16"), _oracle(inp), 2e-2, "grid 512")
+    _compare(_gpu(inp, "bf16"), _oracle(inp), "bf16", "grid 512")
 
 
-def test_bwd_headline_shape():
-    """B8 L4096 D1024 N16 bf16 (the headline shape), every gradient against the
-    oracle's backward over the whole problem."""
-    import oracle
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4])
+def test_bwd_full_size(cfg):
+    """Each full-size workload (the headline B8 L4096 D1024 N16 among them, the
+    variable-length batch, the long dstate-64 sequence with the clip, whose
+    forward the library time-splits) in the benchmark's launch configuration:
+    every element of every gradient, dB and dC included, against the oracle's
+    backward over the whole problem."""
     import torch
     import selective_state_space_scan_amd as ssm
-    w = I.WORKLOADS[2]
-    inp = I.make_inputs(w, I.seed_for(2))
-    cot = I.make_cotangents(w, I.seed_for(2) + 500)
-    dev = to_device(inp, "bf16")
-    y, h, cs = ssm.selective_scan_fwd(dev["x"], dev["delta"], dev["A_log"], dev["B"], dev["C"], dev["D"], None,
-                                      return_chunk_states=True, chunk_len=ssm.bwd_chunk_len(w.dstate))
-    dy = torch.from_numpy(cot["dy"]).cuda().to(torch.bfloat16)
-    g = ssm.selective_scan_bwd(dev["x"], dev["delta"], dev["A_log"], dev["B"], dev["C"], dev["D"], None, dy, cs,
-                               dh_last=torch.from_numpy(cot["dh_last"]).cuda())
+    w = I.WORKLOADS[cfg]
+    inp = I.make_inputs(w, I.seed_for(cfg))
+    cot = I.make_cotangents(w, I.seed_for(cfg) + 500)
+    dev = to_device(inp, w.io)
+    print(f"{w.name}: forward with chunk states, backward", flush=True)
+    y, h, cs = ssm.selective_scan_fwd(dev["x"], dev["delta"], dev["A_log"], dev["B"], dev["C"], dev["D"],
+                                      dev["valid_len"], delta_clamp=w.delta_clamp, return_chunk_states=True,
+                                      chunk_len=ssm.bwd_chunk_len(w.dstate))
+    del y, h
+    dy = torch.from_numpy(cot["dy"]).cuda().to(dev["x"].dtype)
+    g = ssm.selective_scan_bwd(dev["x"], dev["delta"], dev["A_log"], dev["B"], dev["C"], dev["D"], dev["valid_len"],
+                               dy, cs, dh_last=torch.from_numpy(cot["dh_last"]).cuda(), delta_clamp=w.delta_clamp)
     torch.cuda.synchronize()
-    g = {k: (None if v is None else v.float().cpu().numpy().astype(np.float64)) for k, v in g.items()}
-    r = oracle.selective_scan_bwd(inp["x"], inp["delta"], inp["A_log"], inp["B"], inp["C"], inp["D"], cot["dy"],
-                                  dh_last=cot["dh_last"], nthreads=8)
-    worst = {k: rel_err(g[k], r[k]) for k in GRADS if r.get(k) is not None and g.get(k) is not None}
-    print("headline", " ".join(f"{k} {v:.1e}" for k, v in worst.items()), flush=True)
-    assert all(v <= 2e-2 for v in worst.values()), worst
+    g = {k: (None if v is None else to_np64(v)) for k, v in g.items()}
+    del dev, dy, cs
+    r = oracle_bwd(inp, cot["dy"], cot["dh_last"], delta_clamp=w.delta_clamp, nthreads=16)
+    _compare(g, r, w.io, w.name)
+    if inp.get("valid_len") is not None:
+        t = np.arange(w.seqlen)[None, :]
+        pad = t >= np.asarray(inp["valid_len"])[:, None]
+        for k in ("dx", "ddelta", "dB", "dC"):
+            assert np.all(g[k][pad] == 0.0), k
 
 
 def test_bwd_empty_and_degenerate():
@@ -176,7 +187,7 @@ def test_bwd_empty_and_degenerate():
     torch.cuda.synchronize()
     assert g0["dx"].shape == (0, 10, nd)
     w, inp = _case("f32", 16, 77, 1, 16, seed=23)
-    _compare(_gpu(inp, "f32"), _oracle(inp), 1e-4, "one group")
+    _compare(_gpu(inp, "f32"), _oracle(inp), "f32", "one group")
 
 
 def test_bwd_out_of_range_lengths_clamp():
@@ -263,37 +274,3 @@ def test_bwd_outputs_only_4_byte_aligned():
         a = got.contiguous().view(bits).reshape(-1).cpu().numpy()
         b = ref[k].contiguous().view(bits).reshape(-1).cpu().numpy()
         assert np.array_equal(a, b), k
-
-
-@pytest.mark.parametrize("cfg", [1, 3, 4])
-def test_bwd_full_size_sampled_channels(cfg):
-    """The other full-size workloads (the variable-length batch, the long
-    dstate-64 sequence with the clip, which the library time-splits) in the
-    benchmark's launch configuration; the per-channel gradients (dx, ddelta,
-    dA_log, dD, dh0) of sampled 16-channel slices against the oracle's backward
-    run on those channels alone.  dB and dC sum over every channel and are
-    covered at full size by the headline test."""
-    import oracle
-    import torch
-    import selective_state_space_scan_amd as ssm
-    w = I.WORKLOADS[cfg]
-    inp = I.make_inputs(w, I.seed_for(cfg))
-    cot = I.make_cotangents(w, I.seed_for(cfg) + 500)
-    dev = to_device(inp, w.io)
-    y, h, cs = ssm.selective_scan_fwd(dev["x"], dev["delta"], dev["A_log"], dev["B"], dev["C"], dev["D"],
-                                      dev["valid_len"], delta_clamp=w.delta_clamp, return_chunk_states=True,
-                                      chunk_len=ssm.bwd_chunk_len(w.dstate))
-    dy = torch.from_numpy(cot["dy"]).cuda().to(dev["x"].dtype)
-    g = ssm.selective_scan_bwd(dev["x"], dev["delta"], dev["A_log"], dev["B"], dev["C"], dev["D"], dev["valid_len"],
-                               dy, cs, dh_last=torch.from_numpy(cot["dh_last"]).cuda(), delta_clamp=w.delta_clamp)
-    torch.cuda.synchronize()
-    for c0 in (0, w.dim - 16):
-        sl = slice(c0, c0 + 16)
-        r = oracle.selective_scan_bwd(inp["x"][:, :, sl], inp["delta"][:, :, sl], inp["A_log"][sl], inp["B"],
-                                      inp["C"], inp["D"][sl], cot["dy"][:, :, sl], valid_len=inp["valid_len"],
-                                      dh_last=cot["dh_last"][:, sl], delta_clamp=w.delta_clamp, nthreads=16)
-        got = {"dx": g["dx"][:, :, sl], "ddelta": g["ddelta"][:, :, sl], "dA_log": g["dA_log"][sl],
-               "dD": g["dD"][sl], "dh0": g["dh0"][:, sl]}
-        worst = {k: rel_err(to_np64(v), r[k]) for k, v in got.items()}
-        print(w.name, c0, " ".join(f"{k} {v:.1e}" for k, v in worst.items()), flush=True)
-        assert all(v <= tol_for(w.io) for v in worst.values()), worst

@@ -83,7 +83,7 @@ def test_forward_row_at_the_limit(time_parts):
     # the last steps carry the largest offsets: compare them on their own too
     et = rel_err(yg[:, -300:], yr[:, -300:])
     print(f"y {ey:.2e} (last 300 steps {et:.2e}), h_last {eh:.2e}", flush=True)
-    assert ey <= tol_for("bf16") and et <= tol_for("bf16") and eh <= tol_for("bf16")
+    assert ey <= tol_for("bf16", "y") and et <= tol_for("bf16", "y") and eh <= tol_for("bf16", "h_last")
 
 
 def test_backward_row_at_the_limit():
@@ -110,4 +110,4 @@ def test_backward_row_at_the_limit():
            "dh0": g["dh0"][:, sl]}
     worst = {k: rel_err(to_np64(v), ref[k]) for k, v in got.items()}
     print(" ".join(f"{k} {v:.1e}" for k, v in worst.items()), flush=True)
-    assert all(v <= tol_for("bf16") for v in worst.values()), worst
+    assert all(v <= tol_for("bf16", k) for k, v in worst.items()), worst

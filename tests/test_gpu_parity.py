@@ -1,24 +1,25 @@
 """HIP path against the fp64 oracle on the same seeded inputs (needs the GPU).
 
 Tolerance (per output tensor, y and h_last separately):
-max_i |g_i - r_i| / max(|r_i|, rms(r)) <= 1e-4 for fp32 I/O, <= 2e-2 for bf16
-I/O.  Valid-length handling is checked bit for bit."""
+max_i |g_i - r_i| / max(|r_i|, rms(r)) <= 1e-4 for fp32 I/O and for the fp32
+h_last of every workload, <= 2e-2 for the bf16 y of bf16 I/O.  Valid-length
+handling is checked bit for bit."""
 import numpy as np
 import pytest
 
 from conftest import rel_err
-from gpu_util import oracle_full, oracle_rows, run_gpu, to_device, to_np64, tol_for
+from gpu_util import oracle_full, run_gpu, to_device, to_np64, tol_for
 from selective_state_space_scan_amd import inputs as I
 
 pytestmark = pytest.mark.gpu
 
 
-def _check_full(w, inp, with_D=True, label=""):
+def _check_full(w, inp, with_D=True, label="", nthreads=8):
     if not with_D:
         inp = dict(inp, D=None)
     dev = to_device(inp, w.io)
     y, h = run_gpu(dev, delta_clamp=w.delta_clamp)
-    yr, hr = oracle_full(inp, delta_clamp=w.delta_clamp)
+    yr, hr = oracle_full(inp, delta_clamp=w.delta_clamp, nthreads=nthreads)
     yg, hg = to_np64(y), to_np64(h)
     assert np.all(np.isfinite(yg)) and np.all(np.isfinite(hg))
     mask = None
@@ -29,8 +30,7 @@ def _check_full(w, inp, with_D=True, label=""):
     ey, eh = rel_err(yg, yr, mask), rel_err(hg, hr)
     print(f"{label} {w.name} D={with_D}: y err {ey:.3e}  h_last err {eh:.3e}  "
           f"y max abs {np.max(np.abs(yg - yr)):.3e}", flush=True)
-    tol = tol_for(w.io)
-    assert ey <= tol and eh <= tol, (ey, eh)
+    assert ey <= tol_for(w.io, "y") and eh <= tol_for(w.io, "h_last"), (ey, eh)
     return ey, eh
 
 
@@ -54,30 +54,12 @@ def test_configs_reduced_size(cfg, with_D):
 
 
 @pytest.mark.parametrize("cfg", [1, 2, 3, 4])
-def test_configs_full_size_sampled(cfg):
-    """Full-size workloads in the benchmark's launch configuration, checked on
-    sampled channels (each (b, d) row the oracle computes on its own)."""
+def test_configs_full_size(cfg):
+    """Full-size workloads in the benchmark's launch configuration (the
+    library's own time split, D present), every element of y and h_last
+    against the oracle over the whole problem; padded steps of y exactly 0."""
     w = I.WORKLOADS[cfg]
-    inp = I.make_inputs(w, I.seed_for(cfg))
-    dev = to_device(inp, w.io)
-    y, h = run_gpu(dev, delta_clamp=w.delta_clamp)
-    rng = np.random.default_rng(cfg)
-    rows = {(0, 0), (w.batch - 1, w.dim - 1), (0, 15), (w.batch - 1, 16)}
-    for _ in range(20 if cfg != 4 else 10):
-        rows.add((int(rng.integers(w.batch)), int(rng.integers(w.dim))))
-    rows = sorted(rows)
-    yr, hr = oracle_rows(inp, rows, delta_clamp=w.delta_clamp, nthreads=16)
-    yg = np.stack([to_np64(y[b, :, d]) for b, d in rows])
-    hg = np.stack([to_np64(h[b, d]) for b, d in rows])
-    mask = None
-    if inp.get("valid_len") is not None:
-        vl = np.asarray(inp["valid_len"])
-        mask = np.arange(w.seqlen)[None, :] < np.array([vl[b] for b, _ in rows])[:, None]
-        assert np.all(yg[~mask] == 0.0)
-    ey, eh = rel_err(yg, yr, mask), rel_err(hg, hr)
-    print(f"{w.name} sampled {len(rows)} rows: y err {ey:.3e}  h_last err {eh:.3e}", flush=True)
-    assert np.all(np.isfinite(to_np64(y)))
-    assert ey <= tol_for(w.io) and eh <= tol_for(w.io)
+    _check_full(w, I.make_inputs(w, I.seed_for(cfg)), label="full size", nthreads=16)
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])

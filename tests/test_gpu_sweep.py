@@ -78,14 +78,12 @@ def test_sweep_forward_and_backward(case):
     yr, hr, csr = oracle.selective_scan(inp["x"], inp["delta"], inp["A_log"], inp["B"], inp["C"], inp["D"],
                                         valid_len=inp.get("valid_len"), delta_clamp=clamp, chunk_len=cl,
                                         nthreads=8, **kw)
-    tol = tol_for(io)
-    assert rel_err(to_np64(y), yr) <= tol, "y"
-    assert rel_err(to_np64(h), hr) <= tol, "h_last"
-    assert rel_err(to_np64(cs), csr) <= tol, "chunk_states"
+    for k, got, ref in (("y", y, yr), ("h_last", h, hr), ("chunk_states", cs, csr)):
+        assert rel_err(to_np64(got), ref) <= tol_for(io, k), k
     r = oracle.selective_scan_bwd(inp["x"], inp["delta"], inp["A_log"], inp["B"], inp["C"], inp["D"], inp["dy"],
                                   valid_len=inp.get("valid_len"), dh_last=inp["dh_last"], delta_clamp=clamp,
                                   nthreads=8, **kw)
     for k in ("dx", "ddelta", "dA_log", "dB", "dC", "dD", "ddelta_bias", "dz", "dh0"):
         if r.get(k) is None or g.get(k) is None:
             continue
-        assert rel_err(to_np64(g[k]), r[k]) <= tol, k
+        assert rel_err(to_np64(g[k]), r[k]) <= tol_for(io, k), k
