@@ -70,8 +70,14 @@ enum ssm_status {
   SSM_ERR_ALIAS = -3,           /* y or h_last overlaps an input, or y overlaps h_last */
   SSM_ERR_HIP = -4,             /* a HIP runtime or launch error */
   SSM_ERR_NO_DEVICE = -5,       /* no usable GPU at the requested ordinal */
-  SSM_ERR_DEVICE_MISMATCH = -6  /* the calling thread's current device is not the handle's device */
+  SSM_ERR_DEVICE_MISMATCH = -6, /* the calling thread's current device is not the handle's device */
+  SSM_ERR_SCRATCH = -7          /* ssm_selective_scan_fwd_noalloc: the time split asked for needs more than
+                                   SSM_SCAN_NOALLOC_SCRATCH_BYTES */
 };
+
+/* Size of the static device scratch behind ssm_selective_scan_fwd_noalloc
+ * (16 MiB per GPU the library runs on, held until the process ends). */
+#define SSM_SCAN_NOALLOC_SCRATCH_BYTES (16u << 20)
 
 typedef struct ssm_scan_dims {
   int64_t batch;          /* number of rows b */
@@ -182,6 +188,29 @@ int64_t ssm_scan_workspace_bytes(const ssm_scan_dims* dims, int32_t time_parts);
 int ssm_selective_scan_fwd_ex(ssm_scan_t handle, const void* x, const void* delta, const float* A_log, const void* B,
                               const void* C, const float* D, const int32_t* valid_len, void* y, float* h_last,
                               const ssm_scan_dims* dims, const ssm_scan_fwd_extras* extras, void* stream);
+
+/* ssm_selective_scan_fwd_ex for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same computation, the same kernels and bitwise the same
+ * results, but the time split's carries live in a static device array of
+ * SSM_SCAN_NOALLOC_SCRATCH_BYTES that every GPU holds for the life of the
+ * process, so the call allocates nothing (and, like every entry point,
+ * enqueues no copy or memset).  extras may be NULL; its workspace must be
+ * NULL and workspace_bytes 0 (else SSM_ERR_INVALID_ARG).  time_parts = 0
+ * picks the split as ssm_selective_scan_fwd_ex would and runs unsplit if
+ * its carries would not fit the scratch (the automatic split never needs
+ * more than 12 MiB); an explicit time_parts >= 2 whose
+ * ssm_scan_workspace_bytes exceeds SSM_SCAN_NOALLOC_SCRATCH_BYTES returns
+ * SSM_ERR_SCRATCH.  Nothing in the scratch needs to start at zero: each call
+ * writes every carry before reading it.  The scratch is shared by every call
+ * on the same GPU (whatever the handle): calls that may overlap in time on
+ * one GPU (different streams, or graphs replayed concurrently) race on it
+ * and must be serialised by the caller.  Other errors as
+ * ssm_selective_scan_fwd_ex. */
+int ssm_selective_scan_fwd_noalloc(ssm_scan_t handle, const void* x, const void* delta, const float* A_log,
+                                   const void* B, const void* C, const float* D, const int32_t* valid_len, void* y,
+                                   float* h_last, const ssm_scan_dims* dims, const ssm_scan_fwd_extras* extras,
+                                   void* stream);
 
 /* ---- backward --------------------------------------------------------
  *

@@ -20,6 +20,9 @@ SSM_ERR_ALIAS = -3
 SSM_ERR_HIP = -4
 SSM_ERR_NO_DEVICE = -5
 SSM_ERR_DEVICE_MISMATCH = -6
+SSM_ERR_SCRATCH = -7
+
+SSM_SCAN_NOALLOC_SCRATCH_BYTES = 16 << 20
 
 SSM_IO_F32 = 0
 SSM_IO_BF16 = 1
@@ -27,7 +30,8 @@ SSM_IO_BF16 = 1
 # Names declared in include/ssm_scan.h.
 EXPORTED = ("ssm_scan_create", "ssm_selective_scan_fwd", "ssm_selective_scan_fwd_ex", "ssm_scan_chunk_len",
             "ssm_scan_auto_time_parts", "ssm_scan_workspace_bytes", "ssm_scan_bwd_chunk_len",
-            "ssm_scan_bwd_workspace_bytes", "ssm_selective_scan_bwd", "ssm_scan_destroy", "ssm_scan_error_string")
+            "ssm_scan_bwd_workspace_bytes", "ssm_selective_scan_bwd", "ssm_scan_destroy", "ssm_scan_error_string",
+            "ssm_selective_scan_fwd_noalloc")
 
 
 class SsmScanError(RuntimeError):
@@ -119,6 +123,8 @@ def lib() -> ctypes.CDLL:
         L.ssm_selective_scan_fwd_ex.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                                                 ctypes.POINTER(ssm_scan_dims), ctypes.POINTER(ssm_scan_fwd_extras), vp]
         L.ssm_selective_scan_fwd_ex.restype = ctypes.c_int
+        L.ssm_selective_scan_fwd_noalloc.argtypes = L.ssm_selective_scan_fwd_ex.argtypes
+        L.ssm_selective_scan_fwd_noalloc.restype = ctypes.c_int
         L.ssm_scan_chunk_len.argtypes = [ctypes.c_int64]
         L.ssm_scan_chunk_len.restype = ctypes.c_int64
         L.ssm_scan_auto_time_parts.argtypes = [vp, ctypes.POINTER(ssm_scan_dims)]
@@ -169,6 +175,15 @@ def ssm_selective_scan_fwd_ex(handle, x, delta, A_log, B, C, D, valid_len, y, h_
     return lib().ssm_selective_scan_fwd_ex(handle, x, delta, A_log, B, C, D, valid_len, y, h_last,
                                            ctypes.byref(dims), None if extras is None else ctypes.byref(extras),
                                            stream)
+
+
+def ssm_selective_scan_fwd_noalloc(handle, x, delta, A_log, B, C, D, valid_len, y, h_last, dims: ssm_scan_dims,
+                                   extras: ssm_scan_fwd_extras | None, stream) -> int:
+    """The allocation-free entry point (raw pointers; the time split's carries
+    in the library's static scratch); returns the status code."""
+    return lib().ssm_selective_scan_fwd_noalloc(handle, x, delta, A_log, B, C, D, valid_len, y, h_last,
+                                                ctypes.byref(dims), None if extras is None else ctypes.byref(extras),
+                                                stream)
 
 
 def chunk_len(dstate: int) -> int:

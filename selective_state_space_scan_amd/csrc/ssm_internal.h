@@ -10,6 +10,7 @@
 struct ssm_scan_handle_s {
   int device;
   int cu_count;
+  float* scratch;  // this device's copy of the forward's static scratch array
 };
 
 namespace {

@@ -628,6 +628,13 @@ int64_t split_ws_floats(const Split& sp, int64_t nb, int64_t nd, int64_t N) {
 
 }  // namespace
 
+// Scratch of ssm_selective_scan_fwd_noalloc: the time split's carries (the
+// workspace of ssm_selective_scan_fwd_ex), in a static array so that the call
+// allocates nothing.  Every GPU holds its own copy until the process ends; its
+// device address comes from hipGetSymbolAddress at handle creation, since the
+// name denotes a host-side stand-in in host code.
+static __device__ __align__(256) float scratch[SSM_SCAN_NOALLOC_SCRATCH_BYTES / 4];
+
 namespace {
 
 // Parts for an automatic time split: none while the (row, channel group)
@@ -678,10 +685,24 @@ int ssm_scan_create(ssm_scan_t* out, int device_ordinal) {
     return SSM_ERR_HIP;
   }
   if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0) return SSM_ERR_UNSUPPORTED;
+  // This device's address of the scratch array, taken with the device current.
+  int prev = -1;
+  if (hipGetDevice(&prev) != hipSuccess || hipSetDevice(device_ordinal) != hipSuccess) {
+    (void)hipGetLastError();
+    return SSM_ERR_HIP;
+  }
+  void* scratch_ptr = nullptr;
+  const hipError_t sym = hipGetSymbolAddress(&scratch_ptr, HIP_SYMBOL(scratch));
+  const hipError_t back = hipSetDevice(prev);
+  if (sym != hipSuccess || back != hipSuccess || scratch_ptr == nullptr) {
+    (void)hipGetLastError();
+    return SSM_ERR_HIP;
+  }
   ssm_scan_handle_s* h = new (std::nothrow) ssm_scan_handle_s;
   if (h == nullptr) return SSM_ERR_HIP;
   h->device = device_ordinal;
   h->cu_count = prop.multiProcessorCount;
+  h->scratch = static_cast<float*>(scratch_ptr);
   *out = h;
   return SSM_OK;
 }
@@ -707,6 +728,9 @@ const char* ssm_scan_error_string(int code) {
       return "no usable GPU at that ordinal";
     case SSM_ERR_DEVICE_MISMATCH:
       return "the current device is not the handle's device";
+    case SSM_ERR_SCRATCH:
+      return "the time split asked for needs more than the library's static scratch "
+             "(SSM_SCAN_NOALLOC_SCRATCH_BYTES)";
     default:
       return "unknown status code";
   }
@@ -726,12 +750,18 @@ int64_t ssm_scan_workspace_bytes(const ssm_scan_dims* dims, int32_t time_parts) 
   return 4 * split_ws_floats(sp, dims->batch, dims->dim, dims->dstate);
 }
 
-// Checks run in this order: dims, sizes and flags; pointers; alignment;
-// aliasing; the handle; the current device.  Nothing is enqueued unless all
-// pass.
-int ssm_selective_scan_fwd_ex(ssm_scan_t handle, const void* x, const void* delta, const float* A_log, const void* B,
-                              const void* C, const float* D, const int32_t* valid_len, void* y, float* h_last,
-                              const ssm_scan_dims* dims, const ssm_scan_fwd_extras* extras, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The forward behind both entry points.  Checks run in this order: dims,
+// sizes and flags; pointers; alignment; aliasing; the handle; the current
+// device.  Nothing is enqueued unless all pass.  With use_scratch the time
+// split's carries go to the handle's device copy of the static scratch array
+// instead of the caller's workspace (whose fields must then be NULL and 0).
+int fwd_impl(ssm_scan_t handle, const void* x, const void* delta, const float* A_log, const void* B, const void* C,
+             const float* D, const int32_t* valid_len, void* y, float* h_last, const ssm_scan_dims* dims,
+             const ssm_scan_fwd_extras* extras, void* stream, bool use_scratch) {
   if (dims == nullptr) return SSM_ERR_INVALID_ARG;
   const int64_t nb = dims->batch, L = dims->seqlen, nd = dims->dim, N = dims->dstate;
   if (nb < 0 || L < 0 || nd < 0 || N < 0) return SSM_ERR_INVALID_ARG;
@@ -760,11 +790,13 @@ int ssm_selective_scan_fwd_ex(ssm_scan_t handle, const void* x, const void* delt
     return SSM_ERR_INVALID_ARG;
   if (ex.time_parts < 0 || ex.workspace_bytes < 0 || (ex.workspace == nullptr && ex.workspace_bytes != 0))
     return SSM_ERR_INVALID_ARG;
-  // An explicit split needs its workspace; the automatic one is skipped when
-  // the workspace is missing or too small.
+  if (use_scratch && (ex.workspace != nullptr || ex.workspace_bytes != 0)) return SSM_ERR_INVALID_ARG;
+  const int64_t ws_cap = use_scratch ? static_cast<int64_t>(SSM_SCAN_NOALLOC_SCRATCH_BYTES) : ex.workspace_bytes;
+  // An explicit split needs its workspace (or must fit the scratch); the
+  // automatic one is skipped when the workspace is missing or too small.
   if (ex.time_parts >= 2) {
     const Split sp = split_for(L, N, ex.time_parts);
-    if (4 * split_ws_floats(sp, nb, nd, N) > ex.workspace_bytes) return SSM_ERR_INVALID_ARG;
+    if (4 * split_ws_floats(sp, nb, nd, N) > ws_cap) return use_scratch ? SSM_ERR_SCRATCH : SSM_ERR_INVALID_ARG;
   }
 
   const bool empty = (nb == 0 || nd == 0);
@@ -858,7 +890,7 @@ int ssm_selective_scan_fwd_ex(ssm_scan_t handle, const void* x, const void* delt
   int64_t parts = ex.time_parts;
   if (parts == 0) {
     parts = auto_parts(handle, nb, L, nd, N);
-    if (parts >= 2 && 4 * split_ws_floats(split_for(L, N, parts), nb, nd, N) > ex.workspace_bytes) parts = 1;
+    if (parts >= 2 && 4 * split_ws_floats(split_for(L, N, parts), nb, nd, N) > ws_cap) parts = 1;
   }
   // In place (h0 == h_last) the scan runs unsplit: split, the first part's
   // workgroups would read h0 while the last part's, in the same launch, write
@@ -866,7 +898,7 @@ int ssm_selective_scan_fwd_ex(ssm_scan_t handle, const void* x, const void* delt
   if (ex.h0 != nullptr && static_cast<const void*>(ex.h0) == static_cast<const void*>(h_last)) parts = 1;
   const Split sp = split_for(L, N, parts);
   if (static_cast<int64_t>(nb) * (nd / 16) * sp.parts > 0x7fffffffLL) return SSM_ERR_UNSUPPORTED;
-  prm.ws = static_cast<float*>(ex.workspace);
+  prm.ws = use_scratch ? handle->scratch : static_cast<float*>(ex.workspace);
   prm.part_len = sp.part_len;
   prm.n_parts = static_cast<int32_t>(sp.parts);
   const int G = static_cast<int>(N / 16);
@@ -875,10 +907,27 @@ int ssm_selective_scan_fwd_ex(ssm_scan_t handle, const void* x, const void* delt
   return err == hipSuccess ? SSM_OK : SSM_ERR_HIP;
 }
 
+}  // namespace
+
+extern "C" {
+
+int ssm_selective_scan_fwd_ex(ssm_scan_t handle, const void* x, const void* delta, const float* A_log, const void* B,
+                              const void* C, const float* D, const int32_t* valid_len, void* y, float* h_last,
+                              const ssm_scan_dims* dims, const ssm_scan_fwd_extras* extras, void* stream) {
+  return fwd_impl(handle, x, delta, A_log, B, C, D, valid_len, y, h_last, dims, extras, stream, false);
+}
+
+int ssm_selective_scan_fwd_noalloc(ssm_scan_t handle, const void* x, const void* delta, const float* A_log,
+                                   const void* B, const void* C, const float* D, const int32_t* valid_len, void* y,
+                                   float* h_last, const ssm_scan_dims* dims, const ssm_scan_fwd_extras* extras,
+                                   void* stream) {
+  return fwd_impl(handle, x, delta, A_log, B, C, D, valid_len, y, h_last, dims, extras, stream, true);
+}
+
 int ssm_selective_scan_fwd(ssm_scan_t handle, const void* x, const void* delta, const float* A_log, const void* B,
                            const void* C, const float* D, const int32_t* valid_len, void* y, float* h_last,
                            const ssm_scan_dims* dims, void* stream) {
-  return ssm_selective_scan_fwd_ex(handle, x, delta, A_log, B, C, D, valid_len, y, h_last, dims, nullptr, stream);
+  return fwd_impl(handle, x, delta, A_log, B, C, D, valid_len, y, h_last, dims, nullptr, stream, false);
 }
 
 }  // extern "C"

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_error_strings():
-    for code in (0, -1, -2, -3, -4, -5, -6, -99, 5):
+    for code in (0, -1, -2, -3, -4, -5, -6, -7, -99, 5):
         s = ssm.error_string(code)
         assert isinstance(s, str) and s
 
@@ -193,6 +193,46 @@ def test_time_split_checks():
     assert _ex_call(d, E(time_parts=3, workspace=PTRS["y"] - 64, workspace_bytes=need)) == ssm.SSM_ERR_ALIAS
     assert _ex_call(d, E(time_parts=3, workspace=PTRS["h_last"], workspace_bytes=need)) == ssm.SSM_ERR_ALIAS
     assert _ex_call(d, E(time_parts=3, workspace=8 * MB, workspace_bytes=need)) == ssm.SSM_ERR_INVALID_ARG  # handle
+
+
+def _na_call(dims, extras, **over):
+    p = dict(PTRS, **over)
+    return ssm.ssm_selective_scan_fwd_noalloc(None, p["x"], p["delta"], p["A_log"], p["B"], p["C"], p["D"],
+                                              p["valid_len"], p["y"], p["h_last"], dims, extras, None)
+
+
+def test_noalloc_checks():
+    """The allocation-free forward: the checks of the extended entry point, no
+    caller workspace, and explicit splits bounded by the static scratch."""
+    E = ssm.ssm_scan_fwd_extras
+    assert ssm.SSM_SCAN_NOALLOC_SCRATCH_BYTES == 16 << 20
+    d = _dims(batch=2, seqlen=1000, dim=32, dstate=16)
+    bad_x = dict(x=PTRS["x"] + 1)  # a misaligned input: fails after the extras checks
+    assert _na_call(d, None) == ssm.SSM_ERR_INVALID_ARG  # valid: the NULL handle
+    assert _na_call(d, E(time_parts=3)) == ssm.SSM_ERR_INVALID_ARG
+    assert _na_call(d, E(time_parts=3), **bad_x) == ssm.SSM_ERR_UNSUPPORTED  # no workspace needed
+    # a caller workspace is refused
+    need = ssm.workspace_bytes(d, 3)
+    assert _na_call(d, E(time_parts=3, workspace=8 * MB, workspace_bytes=need), **bad_x) == ssm.SSM_ERR_INVALID_ARG
+    assert _na_call(d, E(workspace=8 * MB), **bad_x) == ssm.SSM_ERR_INVALID_ARG
+    assert _na_call(d, E(workspace_bytes=64), **bad_x) == ssm.SSM_ERR_INVALID_ARG
+    # two parts carry one [batch, dim, dstate] block: 64 x 4096 x 16 floats is
+    # exactly the scratch, one more row is too much
+    at = _dims(batch=64, seqlen=256, dim=4096, dstate=16)
+    assert ssm.workspace_bytes(at, 2) == ssm.SSM_SCAN_NOALLOC_SCRATCH_BYTES
+    assert _na_call(at, E(time_parts=2), **bad_x) == ssm.SSM_ERR_UNSUPPORTED
+    over = _dims(batch=65, seqlen=256, dim=4096, dstate=16)
+    assert _na_call(over, E(time_parts=2)) == ssm.SSM_ERR_SCRATCH
+    big = _dims(batch=16, seqlen=32768, dim=2048, dstate=64)
+    assert ssm.workspace_bytes(big, 16) > ssm.SSM_SCAN_NOALLOC_SCRATCH_BYTES
+    assert _na_call(big, E(time_parts=16)) == ssm.SSM_ERR_SCRATCH
+    # the automatic split never fails for size: it runs unsplit instead
+    assert _na_call(big, E(time_parts=0), **bad_x) == ssm.SSM_ERR_UNSUPPORTED
+    assert _na_call(over, None, **bad_x) == ssm.SSM_ERR_UNSUPPORTED
+    # the other checks are those of the extended entry point
+    assert _na_call(d, E(h0=PTRS["h_last"] + 4)) == ssm.SSM_ERR_ALIAS
+    assert _na_call(d, E(chunk_states=8 * MB, chunk_len=6)) == ssm.SSM_ERR_INVALID_ARG
+    assert ssm.error_string(ssm.SSM_ERR_SCRATCH) != ssm.error_string(-99)
 
 
 def test_bwd_checks():
