@@ -21,6 +21,7 @@ its own roofline and the oracle's backward timed on the same workload.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -245,6 +246,10 @@ def main() -> int:
     ap.add_argument("--cpu-threads", type=int, default=0, help="oracle threads (default: min(16, cpus))")
     ap.add_argument("--pass", dest="which", choices=("fwd", "bwd"), default="fwd",
                     help="measure the forward (default) or the backward")
+    ap.add_argument("--combine", choices=("walk", "wave_scan"), default="walk",
+                    help="how a tile's sub-chunks are joined: the serial walk (default) or the log-depth wave scan")
+    ap.add_argument("--dstate", type=int, default=0,
+                    help="override the workload's state count (16, 32 or 64; for the combine comparison)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="instead of the benchmark, run a plain device copy of this many MiB three times "
                          "(reference reading for the HBM byte counters)")
@@ -273,6 +278,8 @@ def main() -> int:
         print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "repeats": 3}))
         return 0
     w = I.WORKLOADS[args.workload]
+    if args.dstate and args.dstate != w.dstate:
+        w = dataclasses.replace(w, dstate=args.dstate, name=f"{w.name}-as-n{args.dstate}")
     inp = I.make_inputs(w, I.seed_for(args.workload))
     if args.which == "bwd":
         return bench_bwd(args, w, inp)
@@ -301,7 +308,8 @@ def main() -> int:
     def step(k: int):
         s = sets[k % len(sets)]
         ssm.selective_scan_fwd(s["x"], s["delta"], A_log, s["B"], s["C"], D, vl, delta_clamp=w.delta_clamp,
-                               y=ys[k % len(sets)], h_last=hs[k % len(sets)], time_parts=parts, workspace=ws)
+                               y=ys[k % len(sets)], h_last=hs[k % len(sets)], time_parts=parts, workspace=ws,
+                               combine=args.combine)
 
     for k in range(args.warmup):
         step(k)
@@ -368,7 +376,7 @@ def main() -> int:
         "hbm_gbps": round(nbytes / (ms_per_step * 1e-3) / 1e9, 1),
         "config": {"workload": w.name, "batch": w.batch, "seqlen": w.seqlen, "dim": w.dim, "dstate": w.dstate,
                    "io": w.io, "state_updates_per_step": updates, "input_copies_rotated": len(sets),
-                   "time_parts": parts},
+                   "time_parts": parts, "combine": args.combine},
         "roofline": roof,
     }
     if peaks is not None:

@@ -151,7 +151,21 @@ int ssm_selective_scan_fwd(ssm_scan_t handle, const void* x, const void* delta, 
  *               at the same time.  With two parts the results are bitwise those
  *               of the unsplit scan; with more, the states entering parts 2 and
  *               later are composed from per-part sums and may differ from
- *               them by rounding. */
+ *               them by rounding.
+ *  combine      how the sub-chunks of a time tile are joined (the second and
+ *               third levels of the pwwt.cn article, section 3.1):
+ *               SSM_COMBINE_WALK (0, the default and the faster on gfx950):
+ *               one lane per (channel, state) carries the state serially
+ *               through every sub-chunk's (a_prod, b_total) in LDS;
+ *               SSM_COMBINE_WAVE_SCAN (1): a log-depth Hillis-Steele scan of
+ *               the pairs across each wave's sub-chunks by cross-lane
+ *               permutes (its section 2.2), then the serial carry through the
+ *               wave totals only.  Equal in exact arithmetic (the combine is
+ *               associative), within rounding otherwise.  Other values:
+ *               SSM_ERR_INVALID_ARG.  The fold kernel of a time split always
+ *               walks. */
+enum ssm_combine { SSM_COMBINE_WALK = 0, SSM_COMBINE_WAVE_SCAN = 1 };
+
 typedef struct ssm_scan_fwd_extras {
   const float* h0;
   const float* delta_bias;
@@ -161,6 +175,7 @@ typedef struct ssm_scan_fwd_extras {
   int32_t time_parts;
   void* workspace;
   int64_t workspace_bytes;
+  int32_t combine;
 } ssm_scan_fwd_extras;
 
 /* The kernel's time tile for this dstate -- the coarsest chunk_len of

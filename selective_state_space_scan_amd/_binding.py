@@ -27,6 +27,9 @@ SSM_SCAN_NOALLOC_SCRATCH_BYTES = 16 << 20
 SSM_IO_F32 = 0
 SSM_IO_BF16 = 1
 
+SSM_COMBINE_WALK = 0
+SSM_COMBINE_WAVE_SCAN = 1
+
 # Names declared in include/ssm_scan.h.
 EXPORTED = ("ssm_scan_create", "ssm_selective_scan_fwd", "ssm_selective_scan_fwd_ex", "ssm_scan_chunk_len",
             "ssm_scan_auto_time_parts", "ssm_scan_workspace_bytes", "ssm_scan_bwd_chunk_len",
@@ -64,6 +67,7 @@ class ssm_scan_fwd_extras(ctypes.Structure):
         ("time_parts", ctypes.c_int32),
         ("workspace", ctypes.c_void_p),
         ("workspace_bytes", ctypes.c_int64),
+        ("combine", ctypes.c_int32),
     ]
 
 
@@ -252,7 +256,7 @@ def _stream_for(stream, dev):
 def selective_scan_fwd(x, delta, A_log, B, C, D=None, valid_len=None, *, delta_softplus: bool = True,
                        delta_clamp=None, y=None, h_last=None, return_h_last: bool = True, h0=None, delta_bias=None,
                        z=None, return_chunk_states: bool = False, chunk_len=None, time_parts=None, workspace=None,
-                       stream=None):
+                       combine: str = "walk", stream=None):
     """Selective-scan forward on the GPU.  Returns ``(y, h_last)``, or
     ``(y, h_last, chunk_states)`` with ``return_chunk_states``.
 
@@ -274,6 +278,10 @@ def selective_scan_fwd(x, delta, A_log, B, C, D=None, valid_len=None, *, delta_s
     batches too small to fill the GPU), 1 never splits, P >= 2 asks for at most
     P parts.  ``workspace`` is an optional contiguous uint8 tensor on x's device
     used as scratch for a split; one is allocated when needed and not given.
+
+    ``combine``: "walk" (default) joins a tile's sub-chunks by a serial carry
+    walk, "wave_scan" by a log-depth scan across each wave's sub-chunks and a
+    walk over the wave totals (the same result within rounding).
     """
     import torch
 
@@ -354,12 +362,15 @@ def selective_scan_fwd(x, delta, A_log, B, C, D=None, valid_len=None, *, delta_s
             elif (workspace.dtype != torch.uint8 or workspace.device != dev or not workspace.is_contiguous()
                   or workspace.numel() < ws_bytes):
                 raise ValueError(f"workspace must be a contiguous uint8 tensor of at least {ws_bytes} bytes on {dev}")
+        comb = {"walk": SSM_COMBINE_WALK, "wave_scan": SSM_COMBINE_WAVE_SCAN}.get(combine)
+        if comb is None:
+            raise ValueError('combine must be "walk" or "wave_scan"')
         extras = None
         if (h0 is not None or delta_bias is not None or z is not None or chunk_states is not None
-                or ws_bytes > 0 or time_parts is not None):
+                or ws_bytes > 0 or time_parts is not None or comb != SSM_COMBINE_WALK):
             extras = ssm_scan_fwd_extras(ptr(h0), ptr(delta_bias), ptr(z), ptr(chunk_states),
                                          cl if chunk_states is not None else 0, parts,
-                                         ptr(workspace) if ws_bytes > 0 else None, ws_bytes)
+                                         ptr(workspace) if ws_bytes > 0 else None, ws_bytes, comb)
         if extras is None:
             rc = ssm_selective_scan_fwd(h, ptr(x), ptr(delta), ptr(A_log), ptr(B), ptr(C), ptr(D), ptr(valid_len),
                                         ptr(y), ptr(h_last), dims, sptr)

@@ -78,7 +78,26 @@ struct FwdParams {
   int32_t clamp;
   float dmin;
   float dmax;
+  int32_t wave_scan;  // the main kernel combines sub-chunks with the log-depth wave scan
 };
+
+// Row exchanges for the log-depth combine across a wave's sub-chunks.  With
+// both operands v, v_permlane16_swap leaves the rows [0, 0, 2, 2] of v in the
+// first operand and [1, 1, 3, 3] in the second; v_permlane32_swap leaves
+// [0, 1, 0, 1] and [2, 3, 2, 3].  s_nop 1 covers the VALU-write ->
+// permlane-read hazard.
+__device__ __forceinline__ void rows_swap16(float v, float& lo, float& hi) {
+  float a = v, b = v;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  lo = a;
+  hi = b;
+}
+__device__ __forceinline__ void rows_swap32(float v, float& lo, float& hi) {
+  float a = v, b = v;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  lo = a;
+  hi = b;
+}
 
 // ---- the kernel ----------------------------------------------------------
 
@@ -90,12 +109,25 @@ constexpr int kMinWavesPerSimd = 4;
 // three 8-wave workgroups share a CU.
 constexpr int kFoldWavesPerSimd = 6;
 
+// Sub-chunks per batch of the carry walk (2, or a multiple of 4): 8 at
+// dstate 16 and 32, 2 at dstate 64, where every thread walks two (channel,
+// state) pairs and larger batches spill.  Measured (B8 L4096 D1024 forward,
+// bf16, single record buffer; us at dstate 16 / 32 / 64): batches of 8
+// 186.0 / 379.5 / 835.6, of 4 186.7 / 384.7 / 773.6, of 2 188.2 / 387.1 /
+// 751.5.
+template <int G>
+constexpr int kWalkBatch = G == 4 ? 2 : 8;
+
 // FOLD: the fold kernel of the time split -- pass 1 and the carry walk only,
 // over parts 0 .. n_parts-2, leaving each part's carry-out (part 0, from h0)
 // or its b_total and delta sum (later parts, from zero) in the workspace.
 // Otherwise the full forward over every part, each starting from the state
 // the workspace gives for its first step.
-template <typename IO, int G, int K, int W, bool SOFTPLUS, bool CLAMP, bool GATE, bool FOLD>
+// WSCAN: the cross-sub-chunk combine as a log-depth (Hillis-Steele) scan of
+// the (a_prod, b_total) pairs across the sub-chunks of each wave, through
+// v_permlane16/32_swap, with only the wave totals walked serially through LDS;
+// otherwise the serial walk over every sub-chunk of the tile.
+template <typename IO, int G, int K, int W, bool SOFTPLUS, bool CLAMP, bool GATE, bool FOLD, bool WSCAN = false>
 __global__ __launch_bounds__(64 * W, FOLD ? kFoldWavesPerSimd : kMinWavesPerSimd) void ssm_fwd_kernel(FwdParams p) {
   constexpr int N = 16 * G;             // states per channel
   constexpr int QR = 4 / G;             // time sub-chunks per wave
@@ -114,16 +146,20 @@ __global__ __launch_bounds__(64 * W, FOLD ? kFoldWavesPerSimd : kMinWavesPerSimd
   // the walk with the incoming state.  Stored as float4 quads,
   // index ((j * N/4 + n/4) * 16 + c) * 4 + n%4, so that a row of 16 lanes
   // writing one quad each, and a walk wave reading 16 channels x 4 states,
-  // both touch 64 consecutive dwords (no bank conflicts).  Two buffers
-  // alternate between tiles, so the next tile's pass 1 may write while the
-  // previous one is still being read.
-  // (The fold kernel has no pass 2 and uses one buffer, with a barrier after
-  // the walk instead.)
-  constexpr int NBUF = FOLD ? 1 : 2;
-  __shared__ __attribute__((aligned(16))) float agg_b[NBUF][AGG];
+  // both touch 64 consecutive dwords (no bank conflicts).  One buffer: after
+  // the walk, a lane reads only its own sub-chunk's slot, and it writes that
+  // slot again only in the next tile's pass 1; every other access (the walk,
+  // the sub-chunk delta sums) lies between the two barriers of a tile.  (Two
+  // alternating buffers: the same time at dstate 16 and 32, 2 % slower at 64,
+  // more registers spilled.)  The fold kernel, which has no pass 2, takes a
+  // barrier after the walk instead.
+  __shared__ __attribute__((aligned(16))) float agg_b[AGG];
+  // WSCAN: each wave's incoming state, per tile, from the walk over the wave
+  // totals (same quad layout as the records, one slot per wave).
+  __shared__ __attribute__((aligned(16))) float wave_in[WSCAN && !FOLD ? W * 16 * N : 4];
   // Sum of delta over each sub-chunk, channel-major (row stride SDS) so that a
   // walk lane reads its channel's sub-chunks as consecutive quads.
-  __shared__ __attribute__((aligned(16))) float agg_sd[NBUF][16 * SDS];
+  __shared__ __attribute__((aligned(16))) float agg_sd[16 * SDS];
   __shared__ __attribute__((aligned(16))) float a2s[16 * NS];  // A * log2(e) for the workgroup's channels
 
   // Workgroup -> (time part, batch row, channel group).  Workgroups are dealt
@@ -276,12 +312,140 @@ __global__ __launch_bounds__(64 * W, FOLD ? kFoldWavesPerSimd : kMinWavesPerSimd
     }
   };
 
+  // Log-depth combine across the wave's QR sub-chunks (WSCAN).  Each lane
+  // holds its sub-chunk's b_total (bt, folded from zero), its delta sum (sd)
+  // and the Abar of its K steps (ab); a_prod is their product.  An inclusive
+  // Hillis-Steele scan over the sub-chunks (rows q*G + g of the wave) combines
+  // each with the one 1, then 2 sub-chunks earlier -- b updated before a --
+  // taking the partner's values from v_permlane16_swap and v_permlane32_swap
+  // (a sub-chunk is 16 lanes at dstate 16, 32 at dstate 32); the delta sums
+  // are scanned alongside.  Each lane parks its
+  // inclusive b in its record slot (the last sub-chunk's is the wave total),
+  // the wave totals are walked serially in time order (W of them per tile,
+  // the carry kept across tiles) leaving each wave's incoming state in
+  // wave_in, and each lane then forms the state after its sub-chunk, with the
+  // inclusive a_prod recomputed as exp2(A log2(e) * inclusive delta sum); its
+  // own incoming state is the one after the sub-chunk before it.
+  // WSCAN: a lane's wave incoming state, its parked inclusive b and A*log2(e)
+  // for states s .. s+3 (valid from the walk until the next tile's pass 1)
+  auto ws_after_own = [&](int s, float4& hw4, float4& bi4, float4& a24) __attribute__((always_inline)) {
+    hw4 = *reinterpret_cast<const float4*>(wave_in + ((w * (N / 4) + 4 * g) * 16 + c) * 4 + s * 16);
+    bi4 = *reinterpret_cast<const float4*>(agg_b + ((j * (N / 4) + 4 * g) * 16 + c) * 4 + s * 16);
+    a24 = *reinterpret_cast<const float4*>(a2s + c * NS + 16 * g + s);
+  };
+  auto wave_scan_combine = [&](const float (&ab)[K][16], float (&bt)[16], float sd, float (&h)[16],
+                               float& sd_incl) __attribute__((always_inline)) {
+    // QR == 4, distance one sub-chunk: rows 1, 2, 3 take rows 0, 1, 2 (rows 1
+    // and 3 from the swap16 pairing, row 2 through swap16 then swap32).
+    // Distance QR/2 sub-chunks: rows 2 and 3 take rows 0 and 1 (swap32).
+    const bool up1 = q >= 1;
+    const bool up2 = r >= 2;
+    auto prev_row = [&](float v) __attribute__((always_inline)) {
+      float lo, hi, lo2, unused;
+      rows_swap16(v, lo, hi);
+      rows_swap32(hi, lo2, unused);
+      return q == 2 ? lo2 : lo;
+    };
+#pragma unroll
+    for (int S = 0; S < 16; ++S) {
+      float a = ab[0][S];
+#pragma unroll
+      for (int i = 1; i < K; ++i) a *= ab[i][S];
+      if constexpr (QR == 4) {
+        const float pa = prev_row(a);
+        const float pb = prev_row(bt[S]);
+        const float nb = __builtin_fmaf(a, pb, bt[S]);
+        const float na = pa * a;
+        bt[S] = up1 ? nb : bt[S];
+        a = up1 ? na : a;
+      }
+      if constexpr (QR >= 2) {
+        float pb, unused;
+        rows_swap32(bt[S], pb, unused);
+        bt[S] = up2 ? __builtin_fmaf(a, pb, bt[S]) : bt[S];
+      }
+    }
+    float sdi = sd;  // inclusive delta sum over the wave's sub-chunks up to this one
+    if constexpr (QR == 4) {
+      const float ps = prev_row(sdi);
+      sdi = up1 ? ps + sdi : sdi;
+    }
+    if constexpr (QR >= 2) {
+      float ps, unused;
+      rows_swap32(sdi, ps, unused);
+      sdi = up2 ? ps + sdi : sdi;
+    }
+    float* const own = agg_b + ((j * (N / 4) + 4 * g) * 16 + c) * 4;
+#pragma unroll
+    for (int s = 0; s < 16; s += 4)
+      *reinterpret_cast<float4*>(own + s * 16) = make_float4(bt[s], bt[s + 1], bt[s + 2], bt[s + 3]);
+    if (q == QR - 1 && g == 0) agg_sd[c * SDS + w] = sdi;
+    __syncthreads();
+    // serial walk over the W wave totals (the last sub-chunk's slot of each
+    // wave), leaving each wave's incoming state in wave_in
+#pragma unroll
+    for (int k = 0; k < PPL; ++k) {
+      if (pair_valid(k)) {
+        int cc, n;
+        pair_of(k, cc, n);
+        const float a2 = a2s[cc * NS + n];
+        float cr = carry[k];
+        const int qoff = ((n / 4) * 16 + cc) * 4 + (n % 4);
+        const float* ptot = agg_b + (QR - 1) * (N / 4) * 64 + qoff;
+        float* pin = wave_in + qoff;
+        const float* psd = agg_sd + cc * SDS;
+#pragma unroll
+        for (int w0 = 0; w0 < W; w0 += 4) {
+          float av[4], bb[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            av[u] = fast_exp2(a2 * psd[w0 + u]);
+            bb[u] = ptot[(w0 + u) * QR * (N / 4) * 64];
+          }
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            pin[(w0 + u) * (N / 4) * 64] = cr;
+            cr = __builtin_fmaf(av[u], cr, bb[u]);
+          }
+        }
+        carry[k] = cr;
+      }
+    }
+    __syncthreads();
+    sd_incl = sdi;
+#pragma unroll
+    for (int s = 0; s < 16; s += 4) {
+      float4 hw4, bi4, a24;
+      ws_after_own(s, hw4, bi4, a24);
+      const float hws[4] = {hw4.x, hw4.y, hw4.z, hw4.w};
+      if constexpr (QR > 1) {
+        const float bis[4] = {bi4.x, bi4.y, bi4.z, bi4.w}, a2v[4] = {a24.x, a24.y, a24.z, a24.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          // the incoming state is the state after the sub-chunk before
+          const float ho = __builtin_fmaf(fast_exp2(a2v[u] * sdi), hws[u], bis[u]);
+          float pv;
+          if constexpr (QR == 4) {
+            pv = prev_row(ho);
+          } else {
+            float unused;
+            rows_swap32(ho, pv, unused);  // rows 2, 3 <- rows 0, 1
+          }
+          h[s + u] = q == 0 ? hws[u] : pv;
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) h[s + u] = hws[u];
+      }
+    }
+  };
+
   // One tile of T steps starting at step t_tile, with its x and delta already
   // in xv/dv.  FULL: every step of the tile is valid; otherwise steps at or
   // beyond len are the identity and y there is +0.  When `prefetch` is set,
   // the next tile's x and delta are requested into nxv/ndv before the work
   // of this tile starts, so their latency hides behind it.
-  auto tile_body = [&]<bool FULL>(int64_t t_tile, int buf, const uint32_t (&xr)[K], const uint32_t (&dr)[K],
+  auto tile_body = [&]<bool FULL>(int64_t t_tile, const uint32_t (&xr)[K], const uint32_t (&dr)[K],
                                   bool prefetch, uint32_t (&nxv)[K], uint32_t (&ndv)[K]) {
     const int64_t left = len - t_tile - j * K;  // valid steps from this lane's first step
     float xv[K], dv[K];
@@ -340,12 +504,17 @@ __global__ __launch_bounds__(64 * W, FOLD ? kFoldWavesPerSimd : kMinWavesPerSimd
       });
     }
 
+    float h[16];  // pass 2's state, from the sub-chunk's incoming state
+    float sd_incl = 0.0f;  // WSCAN: inclusive delta sum over the wave's sub-chunks up to this one
+    if constexpr (WSCAN && !FOLD) {
+      wave_scan_combine(ab, bt, sd, h, sd_incl);
+    } else {
     {
-      float* pb = agg_b[buf] + ((j * (N / 4) + 4 * g) * 16 + c) * 4;
+      float* pb = agg_b + ((j * (N / 4) + 4 * g) * 16 + c) * 4;
 #pragma unroll
       for (int s = 0; s < 16; s += 4)
         *reinterpret_cast<float4*>(pb + s * 16) = make_float4(bt[s], bt[s + 1], bt[s + 2], bt[s + 3]);
-      if (g == 0) agg_sd[buf][c * SDS + j] = sd;
+      if (g == 0) agg_sd[c * SDS + j] = sd;
     }
     __syncthreads();
 
@@ -358,22 +527,29 @@ __global__ __launch_bounds__(64 * W, FOLD ? kFoldWavesPerSimd : kMinWavesPerSimd
         pair_of(k, cc, n);
         const float a2 = a2s[cc * NS + n];
         float cr = carry[k];
-        float* pbw = agg_b[buf] + ((n / 4) * 16 + cc) * 4 + (n % 4);
-        const float* psd = agg_sd[buf] + cc * SDS;
-        // Batches of WB sub-chunks: all LDS reads of a batch are issued
+        float* pbw = agg_b + ((n / 4) * 16 + cc) * 4 + (n % 4);
+        const float* psd = agg_sd + cc * SDS;
+        // Batches of WB sub-chunks: the LDS reads of a batch are issued
         // together and the decays computed off the carry chain, so the
         // serial part is one FMA and one LDS write per sub-chunk.
-        constexpr int WB = SUB < 8 ? SUB : 8;
+        constexpr int WB = kWalkBatch<G>;
+        static_assert(WB == 2 || WB % 4 == 0, "delta sums are read as pairs or quads");
 #pragma unroll
         for (int j0 = 0; j0 < SUB; j0 += WB) {
           float av[WB], bb[WB];
+          if constexpr (WB == 2) {
+            const float2 v = *reinterpret_cast<const float2*>(psd + j0);
+            av[0] = v.x;
+            av[1] = v.y;
+          } else {
 #pragma unroll
-          for (int u = 0; u < WB; u += 4) {
-            const float4 v = *reinterpret_cast<const float4*>(psd + j0 + u);
-            av[u] = v.x;
-            av[u + 1] = v.y;
-            av[u + 2] = v.z;
-            av[u + 3] = v.w;
+            for (int u = 0; u < WB; u += 4) {
+              const float4 v = *reinterpret_cast<const float4*>(psd + j0 + u);
+              av[u] = v.x;
+              av[u + 1] = v.y;
+              av[u + 2] = v.z;
+              av[u + 3] = v.w;
+            }
           }
 #pragma unroll
           for (int u = 0; u < WB; ++u) bb[u] = pbw[(j0 + u) * (N / 4) * 64];
@@ -404,18 +580,15 @@ __global__ __launch_bounds__(64 * W, FOLD ? kFoldWavesPerSimd : kMinWavesPerSimd
         if (pair_valid(k)) {
           int cc, n;
           pair_of(k, cc, n);
-          const float* pbw = agg_b[buf] + ((n / 4) * 16 + cc) * 4 + (n % 4);
+          const float* pbw = agg_b + ((n / 4) * 16 + cc) * 4 + (n % 4);
           for (int jj = clj - 1; jj < SUB; jj += clj)
             store_chunk(ci0 + (jj + 1) / clj - 1, k, jj == SUB - 1 ? carry[k] : pbw[(jj + 1) * (N / 4) * 64]);
         }
       }
     }
     __syncthreads();
-
-    // ---- pass 2: states from the incoming state, readout ----
-    float h[16];
     {
-      const float* pb = agg_b[buf] + ((j * (N / 4) + 4 * g) * 16 + c) * 4;
+      const float* pb = agg_b + ((j * (N / 4) + 4 * g) * 16 + c) * 4;
 #pragma unroll
       for (int s = 0; s < 16; s += 4) {
         const float4 v = *reinterpret_cast<const float4*>(pb + s * 16);
@@ -425,6 +598,9 @@ __global__ __launch_bounds__(64 * W, FOLD ? kFoldWavesPerSimd : kMinWavesPerSimd
         h[s + 3] = v.w;
       }
     }
+    }  // serial walk
+
+    // ---- pass 2: states from the incoming state, readout ----
 #pragma unroll
     for (int i = 0; i < K; ++i) {
       // A fresh name for B so that its broadcasts are not shared with pass 1
@@ -451,6 +627,24 @@ __global__ __launch_bounds__(64 * W, FOLD ? kFoldWavesPerSimd : kMinWavesPerSimd
         if (i < L - t_tile - j * K && (G == 1 || (i % G) == g)) Elem<IO>::store(ry, off_xd, sx, yv);
       }
     }
+    if constexpr (WSCAN && !FOLD) {
+      // chunk-boundary states: the state after a sub-chunk that ends a chunk
+      if (want_chunks && ((j + 1) % clj) == 0) {
+        const int64_t ci = (t_begin + t_tile) / p.chunk_len + (j + 1) / clj - 1;
+        if (ci < n_chunks) {
+          float* dst = p.chunk_states + ((static_cast<int64_t>(b) * n_chunks + ci) * nd + d) * N + 16 * g;
+#pragma unroll
+          for (int s = 0; s < 16; s += 4) {
+            float4 hw4, bi4, a24;
+            ws_after_own(s, hw4, bi4, a24);
+            dst[s] = __builtin_fmaf(fast_exp2(a24.x * sd_incl), hw4.x, bi4.x);
+            dst[s + 1] = __builtin_fmaf(fast_exp2(a24.y * sd_incl), hw4.y, bi4.y);
+            dst[s + 2] = __builtin_fmaf(fast_exp2(a24.z * sd_incl), hw4.z, bi4.z);
+            dst[s + 3] = __builtin_fmaf(fast_exp2(a24.w * sd_incl), hw4.w, bi4.w);
+          }
+        }
+      }
+    }
   };
 
   __syncthreads();  // a2s is written
@@ -458,8 +652,7 @@ __global__ __launch_bounds__(64 * W, FOLD ? kFoldWavesPerSimd : kMinWavesPerSimd
   uint32_t xa[K], da[K], xn[K], dn[K];
   if (nfull > 0) load_xd.template operator()<true>(0, xa, da);
   for (int64_t tile = 0; tile < nfull; ++tile) {
-    tile_body.template operator()<true>(tile * T, FOLD ? 0 : static_cast<int>(tile & 1), xa, da, tile + 1 < nfull,
-                                        xn, dn);
+    tile_body.template operator()<true>(tile * T, xa, da, tile + 1 < nfull, xn, dn);
 #pragma unroll
     for (int i = 0; i < K; ++i) {
       xa[i] = xn[i];
@@ -469,7 +662,7 @@ __global__ __launch_bounds__(64 * W, FOLD ? kFoldWavesPerSimd : kMinWavesPerSimd
   int64_t t_next = nfull * T;
   if (t_next < len) {
     load_xd.template operator()<false>(t_next, xa, da);
-    tile_body.template operator()<false>(t_next, FOLD ? 0 : static_cast<int>(nfull & 1), xa, da, false, xn, dn);
+    tile_body.template operator()<false>(t_next, xa, da, false, xn, dn);
     t_next += T;
   }
   if constexpr (FOLD) {
@@ -544,8 +737,12 @@ hipError_t launch_flags(const FwdParams& prm, hipStream_t stream) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL((ssm_fwd_kernel<IO, G, K, W, SP, CL, GATE, false>),
-                     dim3(static_cast<unsigned>(groups * prm.n_parts)), dim3(64 * W), 0, stream, prm);
+  if (prm.wave_scan)
+    hipLaunchKernelGGL((ssm_fwd_kernel<IO, G, K, W, SP, CL, GATE, false, true>),
+                       dim3(static_cast<unsigned>(groups * prm.n_parts)), dim3(64 * W), 0, stream, prm);
+  else
+    hipLaunchKernelGGL((ssm_fwd_kernel<IO, G, K, W, SP, CL, GATE, false>),
+                       dim3(static_cast<unsigned>(groups * prm.n_parts)), dim3(64 * W), 0, stream, prm);
   return hipGetLastError();
 }
 
@@ -782,8 +979,9 @@ int fwd_impl(ssm_scan_t handle, const void* x, const void* delta, const float* A
   const int64_t esz = dims->io_dtype == SSM_IO_BF16 ? 2 : 4;
   if (L > 0 && L * (N > nd ? N : nd) * esz > 0x7fffffffLL) return SSM_ERR_UNSUPPORTED;
 
-  const ssm_scan_fwd_extras none = {nullptr, nullptr, nullptr, nullptr, 0, 0, nullptr, 0};
+  const ssm_scan_fwd_extras none = {nullptr, nullptr, nullptr, nullptr, 0, 0, nullptr, 0, SSM_COMBINE_WALK};
   const ssm_scan_fwd_extras& ex = extras ? *extras : none;
+  if (ex.combine != SSM_COMBINE_WALK && ex.combine != SSM_COMBINE_WAVE_SCAN) return SSM_ERR_INVALID_ARG;
   // chunk_len: a multiple of the 4-step sub-chunk that divides the tile
   if (ex.chunk_states != nullptr &&
       (ex.chunk_len < 4 || ex.chunk_len % 4 != 0 || tile_steps(N) % ex.chunk_len != 0))
@@ -887,6 +1085,7 @@ int fwd_impl(ssm_scan_t handle, const void* x, const void* delta, const float* A
   prm.clamp = dims->delta_clamp;
   prm.dmin = dims->delta_min;
   prm.dmax = dims->delta_max;
+  prm.wave_scan = ex.combine == SSM_COMBINE_WAVE_SCAN;
   int64_t parts = ex.time_parts;
   if (parts == 0) {
     parts = auto_parts(handle, nb, L, nd, N);

@@ -163,6 +163,11 @@ def test_extras_checks():
     assert _ex_call(_dims(), E(h0=PTRS["h_last"])) == ssm.SSM_ERR_INVALID_ARG  # in place: reaches the handle check
     assert _ex_call(_dims(), E(chunk_states=PTRS["x"], chunk_len=128)) == ssm.SSM_ERR_ALIAS
     assert _ex_call(_dims(), E(chunk_states=PTRS["h_last"], chunk_len=128)) == ssm.SSM_ERR_ALIAS
+    # the combine: walk (0) or wave scan (1)
+    assert _ex_call(_dims(), E(combine=ssm.SSM_COMBINE_WAVE_SCAN)) == ssm.SSM_ERR_INVALID_ARG  # the NULL handle
+    assert _ex_call(_dims(), E(combine=ssm.SSM_COMBINE_WAVE_SCAN), x=PTRS["x"] + 1) == ssm.SSM_ERR_UNSUPPORTED
+    for bad in (2, -1):
+        assert _ex_call(_dims(), E(combine=bad), x=PTRS["x"] + 1) == ssm.SSM_ERR_INVALID_ARG, bad
 
 
 def test_time_split_checks():
