@@ -167,6 +167,40 @@ def cpu_baseline(inp, w, threads: int, min_seconds: float = 1.0) -> dict:
                       f"{threads} threads over (b, d) rows; fp64, gcc -O2)", "host": host_cpu()}
 
 
+LDS_PATTERNS = ("read_b32 consecutive", "write_b32 consecutive", "read_b64 consecutive", "read_b128 consecutive",
+                "write_b128 consecutive", "read_b32 broadcast", "read_b32 stride 2 (two lanes per bank)",
+                "read_b128 16-lane rows broadcast, rows 80 words apart",
+                "read2st64_b32 pair 256 words apart (same bank)", "read2_b32 pair 68 words apart (different banks)",
+                "write2st64_b32 pair 256 words apart (same bank)")
+
+
+def lds_probe(dev, blocks: int = 1024, iters: int = 4096) -> dict:
+    """Launch each LDS access pattern of libssmpeaks.so once, in order (a
+    profiler reads the LDS counters of each dispatch), and report their times."""
+    import ctypes
+
+    import torch
+
+    from selective_state_space_scan_amd import build as B
+    lib = ctypes.CDLL(B.PEAKS_LIB_PATH)
+    lib.ssm_peak_launch.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.ssm_peak_launch.restype = ctypes.c_int
+    stream = torch.cuda.current_stream(dev)
+    out = torch.empty(blocks * 256, dtype=torch.float32, device=dev)
+    res = {"lds_probe": {"blocks": blocks, "waves_per_block": 4, "accesses_per_wave": iters, "patterns": []}}
+    for k, name in enumerate(LDS_PATTERNS):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        rc = lib.ssm_peak_launch(4, None, None, k, out.data_ptr(), blocks, iters, stream.cuda_stream)
+        e1.record(stream)
+        if rc != 0:
+            raise RuntimeError(f"ssm_peak_launch(4, pattern {k}) failed: {rc}")
+        torch.cuda.synchronize()
+        res["lds_probe"]["patterns"].append({"pattern": k, "name": name, "ms": round(e0.elapsed_time(e1), 4)})
+    return res
+
+
 def measure_peaks(dev) -> dict:
     """Peak rates of this GPU from the microbenchmarks in libssmpeaks.so
     (median of 10 timed launches after 3 warm-ups, HIP events on the
@@ -250,6 +284,9 @@ def main() -> int:
                     help="how a tile's sub-chunks are joined: the serial walk (default) or the log-depth wave scan")
     ap.add_argument("--dstate", type=int, default=0,
                     help="override the workload's state count (16, 32 or 64; for the combine comparison)")
+    ap.add_argument("--lds-probe", action="store_true",
+                    help="instead of the benchmark, launch each LDS access pattern of libssmpeaks.so once "
+                         "(reference readings for the LDS instruction and bank-conflict counters)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="instead of the benchmark, run a plain device copy of this many MiB three times "
                          "(reference reading for the HBM byte counters)")
@@ -268,6 +305,9 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("no GPU available", file=sys.stderr)
         return 1
+    if args.lds_probe:
+        print(json.dumps(lds_probe(torch.device("cuda:0"))))
+        return 0
     if args.copy_calibration_mb:
         n = args.copy_calibration_mb << 20
         src = torch.ones(n // 4, dtype=torch.float32, device="cuda:0")

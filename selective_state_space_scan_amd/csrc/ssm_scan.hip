@@ -214,11 +214,22 @@ __global__ __launch_bounds__(64 * W, FOLD ? kFoldWavesPerSimd : kMinWavesPerSimd
   const float dskip = (p.D != nullptr && g == 0) ? p.D[d] : 0.0f;
   const float dbias = (p.delta_bias != nullptr) ? p.delta_bias[d] : 0.0f;
 
-  // The walk lane's (channel, state) pair k: channel fastest.
+  // The walk lane's (channel, state) pair k.  At dstate 16 and 32 each group
+  // of 64 pairs is 16 channels x 4 states, state fastest, so that a wave's
+  // lanes touch 64 consecutive words of a record slot (the LDS serves a
+  // 32-lane half per cycle from 32 banks: with the channel fastest, channels c
+  // and c + 8 shared a bank, 67 conflict cycles per wave and tile; this way 2,
+  // and 1-2 % faster).  At dstate 64 the channel stays fastest: the other
+  // order spills more registers there and is 7 % slower.
   auto pair_of = [&](int k, int& cc, int& n) {
     const int pr = tid + k * NT;
-    cc = pr % 16;
-    n = pr / 16;
+    if constexpr (G == 4) {
+      cc = pr % 16;
+      n = pr / 16;
+    } else {
+      cc = (pr & 63) >> 2;
+      n = 4 * (pr >> 6) + (pr & 3);
+    }
   };
   auto pair_valid = [&](int k) { return PAIRS % NT == 0 || tid + k * NT < PAIRS; };
   // Offset of pair k within the workgroup's 16 x N block of a [.., dim, dstate]

@@ -261,10 +261,15 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
   const float dskip = (p.D != nullptr) ? p.D[d] : 0.0f;
   const float dbias = (p.delta_bias != nullptr) ? p.delta_bias[d] : 0.0f;
 
+  // The walk lane's (channel, state) pair k: each group of 64 pairs is 16
+  // channels x 4 states, state fastest, so that a wave's lanes touch 64
+  // consecutive words of a record slot (with the channel fastest, channels c
+  // and c + 8 shared an LDS bank: 0.3 / 1.3 / 4.1 % slower at dstate
+  // 16 / 32 / 64).
   auto pair_of = [&](int k, int& cc, int& n) {
     const int pr = tid + k * NT;
-    cc = pr % 16;
-    n = pr / 16;
+    cc = (pr & 63) >> 2;
+    n = 4 * (pr >> 6) + (pr & 3);
   };
   auto pair_valid = [&](int k) { return PAIRS % NT == 0 || tid + k * NT < PAIRS; };
   auto pair_offset = [&](int k) {
