@@ -124,3 +124,57 @@ def test_backward_graph_replays():
         assert np.array_equal(_bits(y), _bits(y_ref)), f"replay {i}: y differs"
         for k, v in g_ref.items():
             assert np.array_equal(_bits(g[k]), _bits(v)), f"replay {i}: {k} differs"
+
+
+def test_noalloc_forward_graph_replays():
+    """The allocation-free forward (the time split's carries in the library's
+    static scratch) captured into a graph: each replay equals the eager call,
+    also after eager calls on other inputs have overwritten the scratch."""
+    import torch
+    import selective_state_space_scan_amd as ssm
+    static = _inputs(41, nb=1, L=3000, nd=256, varlen=(2999,))
+    other = _inputs(42, nb=1, L=3000, nd=256, varlen=(3000,))
+    dims = ssm.ssm_scan_dims()
+    dims.batch, dims.seqlen, dims.dim = static["x"].shape
+    dims.dstate = static["A_log"].shape[1]
+    dims.io_dtype, dims.delta_softplus = ssm.SSM_IO_BF16, 1
+    h = ssm._binding.handle_for(torch.cuda.current_device())
+    parts = ssm.auto_time_parts(h, dims)
+    assert parts >= 2  # the scratch is in use
+    ex = ssm.ssm_scan_fwd_extras(None, None, None, None, 0, 0, None, 0)
+
+    def call(d, y, hl, stream):
+        args = [d[k].data_ptr() for k in ("x", "delta", "A_log", "B", "C", "D", "valid_len")]
+        rc = ssm.ssm_selective_scan_fwd_noalloc(h, *args, y.data_ptr(), hl.data_ptr(), dims, ex, stream)
+        assert rc == ssm.SSM_OK, ssm.error_string(rc)
+
+    cur = torch.cuda.current_stream().cuda_stream
+    refs = {}
+    for name, d in (("static", static), ("other", other)):
+        y, hl = torch.empty_like(d["x"]), torch.empty((1, 256, 16), dtype=torch.float32, device="cuda")
+        call(d, y, hl, cur)
+        refs[name] = (y, hl)
+    torch.cuda.synchronize()
+    y = torch.empty_like(static["x"])
+    hl = torch.empty((1, 256, 16), dtype=torch.float32, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            call(static, y, hl, s.cuda_stream)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    y2, h2 = torch.empty_like(y), torch.empty_like(hl)
+    for i in range(4):
+        y.fill_(float("nan"))
+        hl.fill_(float("nan"))
+        call(other, y2, h2, cur)  # rewrites the scratch with another problem's carries
+        torch.cuda.synchronize()
+        if i == 2:
+            _load(static, other)
+        g.replay()
+        torch.cuda.synchronize()
+        want = refs["other"] if i >= 2 else refs["static"]
+        assert np.array_equal(_bits(y), _bits(want[0])), f"replay {i}: y differs"
+        assert np.array_equal(_bits(hl), _bits(want[1])), f"replay {i}: h_last differs"

@@ -1,8 +1,8 @@
 """A seeded sweep over combinations the targeted tests cover one at a time:
 random shapes (ragged lengths, several tiles), dstate 16/32/64, fp32 and bf16
-I/O, padded rows, every forward extra, the clip, and explicit time splits --
-forward and backward against the fp64 oracle, to the same tolerances as the
-targeted tests (1e-4 relative for fp32 I/O, 2e-2 for bf16)."""
+I/O, padded rows, every forward extra, the clip, explicit time splits and
+(every fifth case) the wave-scan combine -- forward and backward against the
+fp64 oracle, to the same per-tensor tolerances as the targeted tests."""
 import dataclasses
 
 import numpy as np
@@ -31,6 +31,10 @@ def _draw(case: int):
     return io, N, nb, L, nd, varlen, use, clamp, parts, rng
 
 
+def _combine(case: int) -> str:
+    return "wave_scan" if case % 5 == 4 else "walk"
+
+
 def _inputs(io, N, nb, L, nd, varlen, rng, seed):
     base = I.WORKLOADS[0] if io == "f32" else I.WORKLOADS[2]
     w = dataclasses.replace(I.small_workload(base, batch=nb, seqlen=L, dim=nd), dstate=N)
@@ -54,7 +58,7 @@ def test_sweep_forward_and_backward(case):
     io, N, nb, L, nd, varlen, use, clamp, parts, rng = _draw(case)
     inp = _inputs(io, N, nb, L, nd, varlen, rng, seed=8000 + case)
     print(f"case {case}: io {io} N {N} nb {nb} L {L} nd {nd} varlen {varlen} use {use} clamp {clamp} "
-          f"parts {parts}", flush=True)
+          f"parts {parts} combine {_combine(case)}", flush=True)
     dev = to_device(inp, io)
     dt = dev["x"].dtype
     ex = {}
@@ -67,7 +71,7 @@ def test_sweep_forward_and_backward(case):
     cl = ssm.bwd_chunk_len(N)
     y, h, cs = ssm.selective_scan_fwd(dev["x"], dev["delta"], dev["A_log"], dev["B"], dev["C"], dev["D"],
                                       dev["valid_len"], delta_clamp=clamp, return_chunk_states=True, chunk_len=cl,
-                                      time_parts=parts, **ex)
+                                      time_parts=parts, combine=_combine(case), **ex)
     dy = torch.from_numpy(inp["dy"]).cuda().to(dt)
     dhl = torch.from_numpy(inp["dh_last"]).cuda()
     g = ssm.selective_scan_bwd(dev["x"], dev["delta"], dev["A_log"], dev["B"], dev["C"], dev["D"],
