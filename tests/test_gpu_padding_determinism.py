@@ -90,6 +90,38 @@ def test_config3_lengths_bit_exact_rows():
         assert np.all(_bits(y)[b, l:] == 0)
 
 
+def test_length_paired_rows_bit_exact():
+    """Rows with their own lengths at exactly two (row, 16-channel) workgroups
+    per CU take the length-paired row order (the longest row shares its CUs
+    with the shortest): each row still equals the row run alone, bitwise,
+    with tied lengths and an empty row among them."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nd = 512
+    nb = 2 * cus // (nd // 16)
+    if nb < 2 or nb > 64 or (2 * cus) % (nd // 16) or cus % 8 or (cus // 8) % (nd // 16):
+        pytest.skip("the pairing needs whole rows per XCD half on this GPU")
+    L = 700
+    w = I.small_workload(I.WORKLOADS[3], batch=nb, seqlen=L, dim=nd)
+    inp = I.make_inputs(w, 4321)
+    vl = np.random.default_rng(5).integers(1, L + 1, size=nb).astype(np.int32)
+    vl[0], vl[1], vl[2], vl[3] = 0, L, 300, 300
+    inp["valid_len"] = vl
+    dev = to_device(inp, w.io)
+    y, h = run_gpu(dev, time_parts=1)
+    for b in range(nb):
+        l = int(vl[b])
+        if l == 0:
+            assert np.all(_bits(y)[b] == 0) and np.all(_bits(h)[b] == 0)
+            continue
+        one = {k: dev[k][b:b + 1, :l].contiguous() for k in ("x", "delta", "B", "C")}
+        one.update(A_log=dev["A_log"], D=dev["D"], valid_len=None)
+        y1, h1 = run_gpu(one, time_parts=1)
+        assert np.array_equal(_bits(y1)[0], _bits(y)[b, :l]), b
+        assert np.array_equal(_bits(h1)[0], _bits(h)[b]), b
+        assert np.all(_bits(y)[b, l:] == 0), b
+
+
 def test_determinism():
     """pwwt.cn section 5.2: the same input twice must give the same bits."""
     w = I.small_workload(I.WORKLOADS[2], batch=4, seqlen=2048, dim=256)
