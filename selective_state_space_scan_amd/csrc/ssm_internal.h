@@ -151,6 +151,49 @@ __device__ __forceinline__ float sum_state_groups(float v) {
   }
 }
 
+// Length-paired rows.  A grid of exactly two (row, channel-group) workgroups
+// per CU, dealt to the 8 XCDs round-robin (XCD = bid % 8, bid / 8 the order
+// within it): the first half of an XCD's workgroups takes one slot of each of
+// its CUs, the second half the other, in the same CU order.  With rows of
+// different lengths, the longer rows go to the first slots in length order
+// and the shorter ones, in reverse, to the second, so that each CU holds one
+// long and one short row; each XCD half still holds whole rows when the
+// channel groups per row divide the CUs per XCD.  The rows (at most 64) are
+// ranked in LDS by every workgroup: longest first, ties by index.  Called by
+// every thread of the workgroup (it contains barriers).
+__device__ __forceinline__ void length_paired_row(int64_t bid, int64_t groups, int n_cg, int nb, int64_t L,
+                                                  const int32_t* valid_len, int32_t* row_lens, int32_t* row_order,
+                                                  int& b, int& cg) {
+  const int half = static_cast<int>(groups / 16);  // CUs per XCD
+  const int x = static_cast<int>(bid % 8), m = static_cast<int>(bid / 8);
+  const int pos = x * half + (m < half ? m : m - half);
+  const int rank = m < half ? pos : static_cast<int>(groups) - 1 - pos;
+  cg = rank % n_cg;
+  const int tid = threadIdx.x;
+  if (tid < nb) {
+    const int64_t v = valid_len[tid];
+    row_lens[tid] = static_cast<int32_t>(v < 0 ? 0 : (v > L ? L : v));
+  }
+  __syncthreads();
+  if (tid < nb) {
+    const int32_t lr = row_lens[tid];
+    int above = 0;
+    for (int o = 0; o < nb; ++o) above += (row_lens[o] > lr || (row_lens[o] == lr && o < tid)) ? 1 : 0;
+    row_order[above] = tid;
+  }
+  __syncthreads();
+  b = row_order[rank / n_cg];
+}
+
+// Whether a grid takes length-paired rows: rows with their own lengths, no
+// time split, exactly two workgroups per CU, whole rows per XCD half, at most
+// 64 rows.
+inline bool use_length_pairing(const void* valid_len, int64_t parts, int64_t nb, int64_t n_cg, int64_t cus) {
+  const int64_t groups = nb * n_cg;
+  return valid_len != nullptr && parts == 1 && nb <= 64 && n_cg > 0 && cus % 8 == 0 && groups == 2 * cus &&
+         (cus / 8) % n_cg == 0;
+}
+
 template <int S, int K>
 struct Unroll {
   template <typename F>

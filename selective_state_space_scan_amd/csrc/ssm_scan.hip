@@ -184,36 +184,9 @@ __global__ __launch_bounds__(64 * W, FOLD ? kFoldWavesPerSimd : kMinWavesPerSimd
   const int part = static_cast<int>(logical / groups);
   int b = static_cast<int>((logical % groups) / p.n_cg);
   int cg = static_cast<int>(logical % p.n_cg);
-  if (!FOLD && p.pair_rows) {
-    // Rows of different lengths, one dispatch round of two workgroups per CU:
-    // within an XCD the first half of its workgroups takes one slot of each of
-    // its CUs, the second half the other, in the same CU order.  Longer rows
-    // go to the first slots in length order and shorter ones, in reverse, to
-    // the second, so that each CU holds one long and one short row (the long
-    // one then runs alone once the short one ends) instead of whichever two
-    // rows its position gave it; each XCD still holds whole rows.
-    const int half = static_cast<int>(per_xcd / 2);  // CUs per XCD
-    const int x = static_cast<int>(bid % 8), m = static_cast<int>(bid / 8);
-    const int pos = x * half + (m < half ? m : m - half);
-    const int rank = m < half ? pos : static_cast<int>(groups) - 1 - pos;
-    cg = rank % p.n_cg;
-    // the row of that rank by length, longest first, ties by index: lane r
-    // ranks row r against the lengths staged in LDS
-    const int tid0 = threadIdx.x;
-    if (tid0 < p.nb) {
-      const int64_t v = p.valid_len[tid0];
-      row_lens[tid0] = static_cast<int32_t>(v < 0 ? 0 : (v > p.L ? p.L : v));
-    }
-    __syncthreads();
-    if (tid0 < p.nb) {
-      const int32_t lr = row_lens[tid0];
-      int above = 0;
-      for (int o = 0; o < p.nb; ++o) above += (row_lens[o] > lr || (row_lens[o] == lr && o < tid0)) ? 1 : 0;
-      row_order[above] = tid0;
-    }
-    __syncthreads();
-    b = row_order[rank / p.n_cg];
-  }
+  // rows of different lengths: the longest row shares its CUs with the
+  // shortest (309 -> 232 us on 16 rows of 128-8192 steps, 512 channels)
+  if (!FOLD && p.pair_rows) length_paired_row(bid, groups, p.n_cg, p.nb, p.L, p.valid_len, row_lens, row_order, b, cg);
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
@@ -1163,17 +1136,7 @@ int fwd_impl(ssm_scan_t handle, const void* x, const void* delta, const float* A
   if (ex.h0 != nullptr && static_cast<const void*>(ex.h0) == static_cast<const void*>(h_last)) parts = 1;
   const Split sp = split_for(L, N, parts);
   if (static_cast<int64_t>(nb) * (nd / 16) * sp.parts > 0x7fffffffLL) return SSM_ERR_UNSUPPORTED;
-  // Length-paired rows (see the kernel): rows with their own lengths, no time
-  // split, exactly two workgroups per CU in one round, whole rows per XCD
-  // half (channel groups dividing the CUs of an XCD), and few enough rows for
-  // each workgroup to rank them.  Measured on the variable-length workload
-  // (16 rows of 128-8192 steps, 512 channels): 309 -> 232 us.
-  {
-    const int64_t cus = handle->cu_count, groups = nb * (nd / 16);
-    if (valid_len != nullptr && sp.parts == 1 && nb <= 64 && cus % 8 == 0 && groups == 2 * cus &&
-        (cus / 8) % (nd / 16) == 0)
-      prm.pair_rows = 1;
-  }
+  prm.pair_rows = use_length_pairing(valid_len, sp.parts, nb, nd / 16, handle->cu_count) ? 1 : 0;
   prm.ws = use_scratch ? handle->scratch : static_cast<float*>(ex.workspace);
   prm.part_len = sp.part_len;
   prm.n_parts = static_cast<int32_t>(sp.parts);

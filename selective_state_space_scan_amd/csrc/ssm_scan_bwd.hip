@@ -88,6 +88,7 @@ struct BwdParams {
   int32_t nb;
   int32_t nd;
   int32_t n_cg;
+  int32_t pair_rows;  // rows of different lengths: pair the longest with the shortest on each CU
   int32_t clamp;
   float dmin;
   float dmax;
@@ -229,8 +230,11 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
   const int64_t per_xcd = total / 8;
   const int64_t logical = (bid < per_xcd * 8) ? (bid % 8) * per_xcd + bid / 8 : bid;
   const int part = static_cast<int>(logical / groups) + (FOLD ? 1 : 0);
-  const int b = static_cast<int>((logical % groups) / p.n_cg);
-  const int cg = static_cast<int>(logical % p.n_cg);
+  int b = static_cast<int>((logical % groups) / p.n_cg);
+  int cg = static_cast<int>(logical % p.n_cg);
+  // rows of different lengths: the longest row shares its CUs with the shortest
+  __shared__ int32_t row_lens[64], row_order[64];
+  if (!FOLD && p.pair_rows) length_paired_row(bid, groups, p.n_cg, p.nb, p.L, p.valid_len, row_lens, row_order, b, cg);
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;
@@ -978,6 +982,9 @@ int ssm_selective_scan_bwd(ssm_scan_t handle, const void* x, const void* delta, 
   prm.nd = static_cast<int32_t>(nd);
   prm.n_cg = static_cast<int32_t>(n_cg);
   prm.clamp = dims->delta_clamp;
+  // four-wave workgroups, two per CU, when unsplit and more than one per CU
+  prm.pair_rows =
+      use_length_pairing(valid_len, parts, nb, n_cg, handle->cu_count) && groups > handle->cu_count ? 1 : 0;
   prm.dmin = dims->delta_min;
   prm.dmax = dims->delta_max;
   const int G = static_cast<int>(N / 16);

@@ -274,3 +274,29 @@ def test_bwd_outputs_only_4_byte_aligned():
         a = got.contiguous().view(bits).reshape(-1).cpu().numpy()
         b = ref[k].contiguous().view(bits).reshape(-1).cpu().numpy()
         assert np.array_equal(a, b), k
+
+
+def test_bwd_length_paired_rows_bit_exact():
+    """The backward at exactly two (row, channel-group) workgroups per CU with
+    rows of their own lengths takes the length-paired row order; without the
+    last row (one group short of the pairing, the same four-wave unsplit
+    kernel otherwise) it does not.  Every per-row gradient (dx, ddelta, dB,
+    dC, dh0) of the other rows is the same bit for bit either way."""
+    import torch
+    import selective_state_space_scan_amd as ssm
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    nd = 512
+    nb = 2 * cus // (nd // 16)
+    if nb < 3 or nb > 64 or (2 * cus) % (nd // 16) or cus % 8 or (cus // 8) % (nd // 16):
+        pytest.skip("the pairing needs whole rows per XCD half on this GPU")
+    T = ssm.bwd_chunk_len(16)
+    L = 9 * T + 5
+    vl = np.random.default_rng(6).integers(1, L + 1, size=nb).astype(np.int32)
+    vl[0], vl[1], vl[2] = 0, L, vl[3]
+    w, inp = _case("bf16", 16, L, nb, nd, seed=61, varlen=vl, extras=False)
+    g = _gpu(inp, "bf16")
+    sub = {k: (v[:nb - 1] if k in ("x", "delta", "B", "C", "dy", "dh_last", "valid_len") else v) for k, v in inp.items()}
+    gs = _gpu(sub, "bf16")
+    for k in ("dx", "ddelta", "dB", "dC", "dh0"):
+        a = g[k][:nb - 1].float().cpu().numpy()
+        assert np.array_equal(a, gs[k].float().cpu().numpy()), k
