@@ -36,6 +36,14 @@
 //    loaded at all.
 //  * With G > 1 the 16-state partial sums of y from the G state-group rows are
 //    added with v_permlane16_swap / v_permlane32_swap in a fixed order.
+//  * The carry walk can be replaced by a log-depth (Hillis-Steele) scan across
+//    each wave's sub-chunks with a walk over the wave totals only
+//    (extras.combine; slower on this GPU, kept as an option).
+//  * Rows of different lengths at exactly two workgroups per CU are dealt so
+//    that each CU holds one long and one short row (length_paired_row).
+//  * Small batches with long sequences split the time axis over workgroups:
+//    a fold kernel over the first parts, then every part from its incoming
+//    state.
 //
 // All arithmetic is fp32; exp is v_exp_f32 (2^x) after a log2(e) prescale.
 
@@ -147,8 +155,9 @@ __global__ __launch_bounds__(64 * W, FOLD ? kFoldWavesPerSimd : kMinWavesPerSimd
   // Per tile and sub-chunk j, channel c, state n: b_total, then overwritten by
   // the walk with the incoming state.  Stored as float4 quads,
   // index ((j * N/4 + n/4) * 16 + c) * 4 + n%4, so that a row of 16 lanes
-  // writing one quad each, and a walk wave reading 16 channels x 4 states,
-  // both touch 64 consecutive dwords (no bank conflicts).  One buffer: after
+  // writes one quad each into 64 consecutive dwords, and a walk wave reading
+  // 16 channels x 4 states touches 64 dwords (consecutive in its lane order
+  // at dstate 16 and 32, see pair_of).  One buffer: after
   // the walk, a lane reads only its own sub-chunk's slot, and it writes that
   // slot again only in the next tile's pass 1; every other access (the walk,
   // the sub-chunk delta sums) lies between the two barriers of a tile.  (Two
