@@ -90,18 +90,19 @@ def test_config3_lengths_bit_exact_rows():
         assert np.all(_bits(y)[b, l:] == 0)
 
 
-def test_length_paired_rows_bit_exact():
+@pytest.mark.parametrize("nd", [512, 128])
+def test_length_paired_rows_bit_exact(nd):
     """Rows with their own lengths at exactly two (row, 16-channel) workgroups
     per CU take the length-paired row order (the longest row shares its CUs
     with the shortest): each row still equals the row run alone, bitwise,
-    with tied lengths and an empty row among them."""
+    with tied lengths and an empty row among them (16 rows of 512 channels,
+    and 64 rows of 128, the most rows the pairing ranks)."""
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    nd = 512
     nb = 2 * cus // (nd // 16)
     if nb < 2 or nb > 64 or (2 * cus) % (nd // 16) or cus % 8 or (cus // 8) % (nd // 16):
         pytest.skip("the pairing needs whole rows per XCD half on this GPU")
-    L = 700
+    L = 700 if nb <= 16 else 300
     w = I.small_workload(I.WORKLOADS[3], batch=nb, seqlen=L, dim=nd)
     inp = I.make_inputs(w, 4321)
     vl = np.random.default_rng(5).integers(1, L + 1, size=nb).astype(np.int32)
