@@ -95,7 +95,8 @@ def test_auto_split_small_batch_long_sequence():
     y, h, cs = _run(inp, "bf16", None, clamp=(1e-3, 0.1))
     yr, hr, csr = oracle.selective_scan(inp["x"], inp["delta"], inp["A_log"], inp["B"], inp["C"], inp["D"],
                                         delta_clamp=(1e-3, 0.1), chunk_len=ssm.chunk_len(64), nthreads=8)
-    assert rel_err(to_np64(y), yr) <= 2e-2 and rel_err(to_np64(h), hr) <= 2e-2 and rel_err(to_np64(cs), csr) <= 2e-2
+    assert rel_err(to_np64(y), yr) <= tol_for("bf16", "y") and rel_err(to_np64(h), hr) <= tol_for("bf16", "h_last")
+    assert rel_err(to_np64(cs), csr) <= tol_for("bf16", "chunk_states")
     # the same call without a split agrees to rounding
     y1, h1, _ = _run(inp, "bf16", 1, clamp=(1e-3, 0.1))
     assert rel_err(to_np64(h), to_np64(h1)) <= 1e-5
