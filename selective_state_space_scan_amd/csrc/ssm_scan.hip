@@ -121,10 +121,10 @@ constexpr int kFoldWavesPerSimd = 6;
 
 // Sub-chunks per batch of the carry walk (2, or a multiple of 4): 8 at
 // dstate 16 and 32, 2 at dstate 64, where every thread walks two (channel,
-// state) pairs and larger batches spill.  Measured (B8 L4096 D1024 forward,
-// bf16, single record buffer; us at dstate 16 / 32 / 64): batches of 8
-// 186.0 / 379.5 / 835.6, of 4 186.7 / 384.7 / 773.6, of 2 188.2 / 387.1 /
-// 751.5.
+// state) pairs.  Measured (B8 L4096 D1024 forward, bf16, single record
+// buffer; us at dstate 16 / 32 / 64): batches of 8 186.0 / 379.5 / 835.6, of 4
+// 186.7 / 384.7 / 773.6, of 2 188.2 / 387.1 / 751.5; on the current sources
+// at dstate 64, 712 / 706 / 695.
 template <int G>
 constexpr int kWalkBatch = G == 4 ? 2 : 8;
 
@@ -156,8 +156,8 @@ __global__ __launch_bounds__(64 * W, FOLD ? kFoldWavesPerSimd : kMinWavesPerSimd
   // the walk with the incoming state.  Stored as float4 quads,
   // index ((j * N/4 + n/4) * 16 + c) * 4 + n%4, so that a row of 16 lanes
   // writes one quad each into 64 consecutive dwords, and a walk wave reading
-  // 16 channels x 4 states touches 64 dwords (consecutive in its lane order
-  // at dstate 16 and 32, see pair_of).  One buffer: after
+  // 16 channels x 4 states touches 64 consecutive dwords (see pair_of).
+  // One buffer: after
   // the walk, a lane reads only its own sub-chunk's slot, and it writes that
   // slot again only in the next tile's pass 1; every other access (the walk,
   // the sub-chunk delta sums) lies between the two barriers of a tile.  (Two
@@ -228,22 +228,16 @@ __global__ __launch_bounds__(64 * W, FOLD ? kFoldWavesPerSimd : kMinWavesPerSimd
   const float dskip = (p.D != nullptr && g == 0) ? p.D[d] : 0.0f;
   const float dbias = (p.delta_bias != nullptr) ? p.delta_bias[d] : 0.0f;
 
-  // The walk lane's (channel, state) pair k.  At dstate 16 and 32 each group
-  // of 64 pairs is 16 channels x 4 states, state fastest, so that a wave's
-  // lanes touch 64 consecutive words of a record slot (the LDS serves a
-  // 32-lane half per cycle from 32 banks: with the channel fastest, channels c
-  // and c + 8 shared a bank, 67 conflict cycles per wave and tile; this way 2,
-  // and 1-2 % faster).  At dstate 64 the channel stays fastest: the other
-  // order spills more registers there and is 7 % slower.
+  // The walk lane's (channel, state) pair k: each group of 64 pairs is 16
+  // channels x 4 states, state fastest, so that a wave's lanes touch 64
+  // consecutive words of a record slot (the LDS serves a 32-lane half per
+  // cycle from 32 banks: with the channel fastest, channels c and c + 8 shared
+  // a bank, 67 conflict cycles per wave and tile at dstate 16; this way 2, and
+  // 1-2 % faster at every dstate).
   auto pair_of = [&](int k, int& cc, int& n) {
     const int pr = tid + k * NT;
-    if constexpr (G == 4) {
-      cc = pr % 16;
-      n = pr / 16;
-    } else {
-      cc = (pr & 63) >> 2;
-      n = 4 * (pr >> 6) + (pr & 3);
-    }
+    cc = (pr & 63) >> 2;
+    n = 4 * (pr >> 6) + (pr & 3);
   };
   auto pair_valid = [&](int k) { return PAIRS % NT == 0 || tid + k * NT < PAIRS; };
   // Offset of pair k within the workgroup's 16 x N block of a [.., dim, dstate]
@@ -695,15 +689,24 @@ __global__ __launch_bounds__(64 * W, FOLD ? kFoldWavesPerSimd : kMinWavesPerSimd
   };
 
   __syncthreads();  // a2s is written
+  // At dstate 16 the next tile's x and delta are requested before the work of
+  // the current tile (1 % faster than loading them at its top).  At 32 and 64
+  // the registers they occupy across the tile made the compiler spill (24 and
+  // 80 bytes per lane); there each tile loads its own at its top: 1 % and 2 %
+  // faster (the fold kernel too, though it does not spill either way).
+  constexpr bool kPrefetch = G == 1;
   const int64_t nfull = len / T;
   uint32_t xa[K], da[K], xn[K], dn[K];
-  if (nfull > 0) load_xd.template operator()<true>(0, xa, da);
+  if (kPrefetch && nfull > 0) load_xd.template operator()<true>(0, xa, da);
   for (int64_t tile = 0; tile < nfull; ++tile) {
-    tile_body.template operator()<true>(tile * T, xa, da, tile + 1 < nfull, xn, dn);
+    if constexpr (!kPrefetch) load_xd.template operator()<true>(tile * T, xa, da);
+    tile_body.template operator()<true>(tile * T, xa, da, kPrefetch && tile + 1 < nfull, xn, dn);
+    if constexpr (kPrefetch) {
 #pragma unroll
-    for (int i = 0; i < K; ++i) {
-      xa[i] = xn[i];
-      da[i] = dn[i];
+      for (int i = 0; i < K; ++i) {
+        xa[i] = xn[i];
+        da[i] = dn[i];
+      }
     }
   }
   int64_t t_next = nfull * T;
