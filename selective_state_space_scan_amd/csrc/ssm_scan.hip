@@ -15,7 +15,9 @@
 //    SUB = W*(4/G) sub-chunks of K steps.
 //  * Pass 1 (per lane, serial over K steps): Abar = exp2(delta*A*log2e) for
 //    each state, kept in registers; the sub-chunk's folded b_total and its
-//    sum of delta go to LDS.
+//    sum of delta go to LDS.  The G state-group rows of a sub-chunk split the
+//    per-(step, channel) work -- loading x and delta, softplus, u = delta*x --
+//    K/G steps each and exchange the results across rows.
 //  * Carry walk: one lane per (channel, state) walks the SUB sub-chunks of the
 //    tile in time order with the pair (a_prod, b_total), a_prod =
 //    exp2(A*log2e*sum(delta)), leaving each sub-chunk's incoming state in LDS
@@ -317,9 +319,15 @@ __global__ __launch_bounds__(64 * W, FOLD ? kFoldWavesPerSimd : kMinWavesPerSimd
   const uint32_t off_xd = static_cast<uint32_t>((j * K * nd + d) * E);
   const uint32_t off_bc = static_cast<uint32_t>((j * K * N + 16 * g + c) * E);
 
-  // x and delta of the lane's K steps in the tile starting at t_tile, as the
-  // loaded bits (widened to fp32 where they are used, so that a prefetch does
-  // not wait for its data on the spot).  Steps at or beyond len read as 0
+  // x and delta are loaded and discretised once per (step, channel): the G
+  // state-group rows of a sub-chunk share its steps, so row g takes steps
+  // g*KG .. g*KG + KG-1 and the rows exchange the results (share_rows).
+  constexpr int KG = K / G;
+  static_assert(KG * G == K, "each state-group row discretises K / G steps");
+  const uint32_t off_xd_own = off_xd + static_cast<uint32_t>(g * KG * nd * E);
+  // x and delta of the lane's own KG steps in the tile starting at t_tile, as
+  // the loaded bits (widened to fp32 where they are used, so that a prefetch
+  // does not wait for its data on the spot).  Steps at or beyond len read as 0
   // (never loaded).
   auto load_raw = [](rsrc_t r, uint32_t voff, uint32_t soff) -> uint32_t {
     if constexpr (E == 2)
@@ -328,14 +336,32 @@ __global__ __launch_bounds__(64 * W, FOLD ? kFoldWavesPerSimd : kMinWavesPerSimd
       return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kCached);
   };
   auto widen = [](uint32_t u) -> float { return __builtin_bit_cast(float, E == 2 ? u << 16 : u); };
-  auto load_xd = [&]<bool FULL>(int64_t t_tile, uint32_t (&xr)[K], uint32_t (&dr)[K]) {
+  auto load_xd = [&]<bool FULL>(int64_t t_tile, uint32_t (&xr)[KG], uint32_t (&dr)[KG]) {
     const int64_t left = len - t_tile - j * K;
 #pragma unroll
-    for (int i = 0; i < K; ++i) {
-      const bool ok = FULL || i < left;
-      const uint32_t sx = static_cast<uint32_t>((t_tile + i) * xd_step);
-      xr[i] = ok ? load_raw(rx, off_xd, sx) : 0u;
-      dr[i] = ok ? load_raw(rd, off_xd, sx) : 0u;
+    for (int m = 0; m < KG; ++m) {
+      const bool ok = FULL || g * KG + m < left;
+      const uint32_t sx = static_cast<uint32_t>((t_tile + m) * xd_step);
+      xr[m] = ok ? load_raw(rx, off_xd_own, sx) : 0u;
+      dr[m] = ok ? load_raw(rd, off_xd_own, sx) : 0u;
+    }
+  };
+  // The values of all K steps of the sub-chunk from the rows that computed
+  // them (own: this lane's KG steps): at G = 2 the row pair exchanges through
+  // v_permlane16_swap; at G = 4 each row holds one step and the four are
+  // gathered with one v_permlane16_swap and two v_permlane32_swap.
+  auto share_rows = [](const float (&own)[KG], float (&all)[K]) __attribute__((always_inline)) {
+    if constexpr (G == 1) {
+#pragma unroll
+      for (int i = 0; i < K; ++i) all[i] = own[i];
+    } else if constexpr (G == 2) {
+#pragma unroll
+      for (int m = 0; m < KG; ++m) rows_swap16(own[m], all[m], all[KG + m]);  // rows 2q and 2q+1
+    } else {
+      float lo, hi;
+      rows_swap16(own[0], lo, hi);   // rows [0, 0, 2, 2] and [1, 1, 3, 3]
+      rows_swap32(lo, all[0], all[2]);
+      rows_swap32(hi, all[1], all[3]);
     }
   };
 
@@ -467,20 +493,14 @@ __global__ __launch_bounds__(64 * W, FOLD ? kFoldWavesPerSimd : kMinWavesPerSimd
     }
   };
 
-  // One tile of T steps starting at step t_tile, with its x and delta already
-  // in xv/dv.  FULL: every step of the tile is valid; otherwise steps at or
-  // beyond len are the identity and y there is +0.  When `prefetch` is set,
-  // the next tile's x and delta are requested into nxv/ndv before the work
-  // of this tile starts, so their latency hides behind it.
-  auto tile_body = [&]<bool FULL>(int64_t t_tile, const uint32_t (&xr)[K], const uint32_t (&dr)[K],
-                                  bool prefetch, uint32_t (&nxv)[K], uint32_t (&ndv)[K]) {
+  // One tile of T steps starting at step t_tile, with the lane's own x and
+  // delta already in xr/dr.  FULL: every step of the tile is valid; otherwise
+  // steps at or beyond len are the identity and y there is +0.  When
+  // `prefetch` is set, the next tile's x and delta are requested into nxv/ndv
+  // before the work of this tile starts, so their latency hides behind it.
+  auto tile_body = [&]<bool FULL>(int64_t t_tile, const uint32_t (&xr)[KG], const uint32_t (&dr)[KG],
+                                  bool prefetch, uint32_t (&nxv)[KG], uint32_t (&ndv)[KG]) {
     const int64_t left = len - t_tile - j * K;  // valid steps from this lane's first step
-    float xv[K], dv[K];
-#pragma unroll
-    for (int i = 0; i < K; ++i) {
-      xv[i] = widen(xr[i]);
-      dv[i] = widen(dr[i]);
-    }
     float bv[K], cv[K];
 #pragma unroll
     for (int i = 0; i < K; ++i) {
@@ -505,20 +525,28 @@ __global__ __launch_bounds__(64 * W, FOLD ? kFoldWavesPerSimd : kMinWavesPerSimd
 
     // ---- pass 1: discretise, cache Abar, fold the sub-chunk ----
     float ab[K][16];
-    float u[K];
     float bt[16];
-    float sd = 0.0f;
-    float dls[K];
+    float dls[K], u[K], xv[K];
+    {
+      // delta of the lane's own steps first: covers the B/C load latency
+      float dlo[KG], uo[KG], xo[KG];
 #pragma unroll
-    for (int i = 0; i < K; ++i) {  // delta for all K steps first: covers the B/C load latency
-      float dl = dv[i] + dbias;
-      if constexpr (SOFTPLUS) dl = softplus_f32(dl);
-      if constexpr (CLAMP) dl = __builtin_amdgcn_fmed3f(dl, p.dmin, p.dmax);
-      if constexpr (!FULL) dl = (i < left) ? dl : 0.0f;  // padded step: delta = 0 -> Abar = 1
-      dls[i] = dl;
-      u[i] = dl * xv[i];
-      sd += dl;
+      for (int m = 0; m < KG; ++m) {
+        float dl = widen(dr[m]) + dbias;
+        if constexpr (SOFTPLUS) dl = softplus_f32(dl);
+        if constexpr (CLAMP) dl = __builtin_amdgcn_fmed3f(dl, p.dmin, p.dmax);
+        if constexpr (!FULL) dl = (g * KG + m < left) ? dl : 0.0f;  // padded step: delta = 0 -> Abar = 1
+        xo[m] = widen(xr[m]);
+        dlo[m] = dl;
+        uo[m] = dl * xo[m];
+      }
+      share_rows(dlo, dls);
+      share_rows(uo, u);
+      share_rows(xo, xv);
     }
+    float sd = 0.0f;
+#pragma unroll
+    for (int i = 0; i < K; ++i) sd += dls[i];
 #pragma unroll
     for (int i = 0; i < K; ++i) {
       const float dl = dls[i];
@@ -696,16 +724,16 @@ __global__ __launch_bounds__(64 * W, FOLD ? kFoldWavesPerSimd : kMinWavesPerSimd
   // faster (the fold kernel too, though it does not spill either way).
   constexpr bool kPrefetch = G == 1;
   const int64_t nfull = len / T;
-  uint32_t xa[K], da[K], xn[K], dn[K];
+  uint32_t xa[KG], da[KG], xn[KG], dn[KG];
   if (kPrefetch && nfull > 0) load_xd.template operator()<true>(0, xa, da);
   for (int64_t tile = 0; tile < nfull; ++tile) {
     if constexpr (!kPrefetch) load_xd.template operator()<true>(tile * T, xa, da);
     tile_body.template operator()<true>(tile * T, xa, da, kPrefetch && tile + 1 < nfull, xn, dn);
     if constexpr (kPrefetch) {
 #pragma unroll
-      for (int i = 0; i < K; ++i) {
-        xa[i] = xn[i];
-        da[i] = dn[i];
+      for (int m = 0; m < KG; ++m) {
+        xa[m] = xn[m];
+        da[m] = dn[m];
       }
     }
   }
