@@ -151,6 +151,23 @@ __device__ __forceinline__ float sum_state_groups(float v) {
   }
 }
 
+// Row exchanges between the four 16-lane rows of a wave.  With both operands
+// v, v_permlane16_swap leaves the rows [0, 0, 2, 2] of v in the first operand
+// and [1, 1, 3, 3] in the second; v_permlane32_swap leaves [0, 1, 0, 1] and
+// [2, 3, 2, 3].  s_nop 1 covers the VALU-write -> permlane-read hazard.
+__device__ __forceinline__ void rows_swap16(float v, float& lo, float& hi) {
+  float a = v, b = v;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  lo = a;
+  hi = b;
+}
+__device__ __forceinline__ void rows_swap32(float v, float& lo, float& hi) {
+  float a = v, b = v;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+  lo = a;
+  hi = b;
+}
+
 // Length-paired rows.  A grid of exactly two (row, channel-group) workgroups
 // per CU, dealt to the 8 XCDs round-robin (XCD = bid % 8, bid / 8 the order
 // within it): the first half of an XCD's workgroups takes one slot of each of

@@ -93,24 +93,6 @@ struct FwdParams {
   int32_t pair_rows;  // rows of different lengths: pair the longest with the shortest on each CU
 };
 
-// Row exchanges for the log-depth combine across a wave's sub-chunks.  With
-// both operands v, v_permlane16_swap leaves the rows [0, 0, 2, 2] of v in the
-// first operand and [1, 1, 3, 3] in the second; v_permlane32_swap leaves
-// [0, 1, 0, 1] and [2, 3, 2, 3].  s_nop 1 covers the VALU-write ->
-// permlane-read hazard.
-__device__ __forceinline__ void rows_swap16(float v, float& lo, float& hi) {
-  float a = v, b = v;
-  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-  lo = a;
-  hi = b;
-}
-__device__ __forceinline__ void rows_swap32(float v, float& lo, float& hi) {
-  float a = v, b = v;
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-  lo = a;
-  hi = b;
-}
-
 // ---- the kernel ----------------------------------------------------------
 
 // 128 VGPRs, so that two 8-wave workgroups share a CU (4 waves per SIMD).

@@ -329,6 +329,23 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
   const rsrc_t rb = make_rsrc(static_cast<const char*>(p.B) + bc_base, bc_row);
   const rsrc_t rc = make_rsrc(static_cast<const char*>(p.C) + bc_base, bc_row);
   const uint32_t off_xd = static_cast<uint32_t>((j * K * nd + d) * E);
+  // The 2 (dstate 32) or 4 (dstate 64) state-group rows of a sub-chunk share
+  // its K = 2 steps: a lane loads x, delta, dy, z and runs softplus, the clip
+  // and the gate only for its own step (row r takes step r % 2), and the rows
+  // exchange the results with v_permlane16_swap (rows [0, 0, 2, 2] hold step
+  // 0 afterwards, rows [1, 1, 3, 3] step 1).  At dstate 16 a lane has both.
+  constexpr int KS = G == 1 ? K : 1;  // steps a lane discretises
+  static_assert(K == 2, "the row exchange pairs rows 2q and 2q + 1 over two steps");
+  auto own_step = [&](int m) { return G == 1 ? m : (r & 1); };
+  const uint32_t off_xd_own = off_xd + static_cast<uint32_t>(G == 1 ? 0 : (r & 1) * nd * E);
+  auto share_rows = [](const float (&own)[KS], float (&all)[K]) __attribute__((always_inline)) {
+    if constexpr (G == 1) {
+#pragma unroll
+      for (int i = 0; i < K; ++i) all[i] = own[i];
+    } else {
+      rows_swap16(own[0], all[0], all[1]);
+    }
+  };
   const uint32_t off_bc = static_cast<uint32_t>((j * K * N + 16 * g + c) * E);
   // dB / dC partials of this channel group: [n_cg, nb, L, N], from the part's first step
   float* const wdB = p.ws_dB + ((static_cast<int64_t>(cg) * p.nb + b) * p.L + t_begin) * N;
@@ -377,7 +394,8 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
     // without per-lane conditions, so that its loads issue together instead
     // of one masked branch (and one wait) per load.
     const bool full = t_tile + T <= len;  // uniform over the workgroup
-    float xv[K], dlr[K], dyv[K], zv[K], bv[K], cv[K];
+    // x, delta, dy, z: the lane's own steps only (KS of them, see own_step)
+    float xo[KS], dlr[KS], dyo[KS], zo[KS], bv[K], cv[K];
     if (full) {
       // (B and C first: a different order from the masked loads below keeps
       // the compiler from merging the two paths' last loads into one block)
@@ -388,24 +406,28 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
         bv[i] = !FOLD ? Elem<IO>::template load<0>(rb, off_bc, sb) : 0.0f;
       }
 #pragma unroll
-      for (int i = 0; i < K; ++i) {
-        const uint32_t sx = static_cast<uint32_t>((t_tile + i) * xd_step);
+      for (int m = 0; m < KS; ++m) {
+        const uint32_t sx = static_cast<uint32_t>((t_tile + m) * xd_step);
         // the fold needs neither x nor B (only the adjoint input dyp * C)
-        xv[i] = !FOLD ? Elem<IO>::template load<kCached>(rx, off_xd, sx) : 0.0f;
-        dlr[i] = Elem<IO>::template load<kCached>(rd, off_xd, sx);
-        dyv[i] = Elem<IO>::template load<kCached>(rdy, off_xd, sx);
-        zv[i] = GATE ? Elem<IO>::template load<kCached>(rz, off_xd, sx) : 0.0f;
+        xo[m] = !FOLD ? Elem<IO>::template load<kCached>(rx, off_xd_own, sx) : 0.0f;
+        dlr[m] = Elem<IO>::template load<kCached>(rd, off_xd_own, sx);
+        dyo[m] = Elem<IO>::template load<kCached>(rdy, off_xd_own, sx);
+        zo[m] = GATE ? Elem<IO>::template load<kCached>(rz, off_xd_own, sx) : 0.0f;
       }
     } else {
 #pragma unroll
+      for (int m = 0; m < KS; ++m) {
+        const bool ok = own_step(m) < left;
+        const uint32_t sx = static_cast<uint32_t>((t_tile + m) * xd_step);
+        xo[m] = (ok && !FOLD) ? Elem<IO>::template load<kCached>(rx, off_xd_own, sx) : 0.0f;
+        dlr[m] = ok ? Elem<IO>::template load<kCached>(rd, off_xd_own, sx) : 0.0f;
+        dyo[m] = ok ? Elem<IO>::template load<kCached>(rdy, off_xd_own, sx) : 0.0f;
+        zo[m] = (GATE && ok) ? Elem<IO>::template load<kCached>(rz, off_xd_own, sx) : 0.0f;
+      }
+#pragma unroll
       for (int i = 0; i < K; ++i) {
         const bool ok = i < left;
-        const uint32_t sx = static_cast<uint32_t>((t_tile + i) * xd_step);
         const uint32_t sb = static_cast<uint32_t>((t_tile + i) * bc_step);
-        xv[i] = (ok && !FOLD) ? Elem<IO>::template load<kCached>(rx, off_xd, sx) : 0.0f;
-        dlr[i] = ok ? Elem<IO>::template load<kCached>(rd, off_xd, sx) : 0.0f;
-        dyv[i] = ok ? Elem<IO>::template load<kCached>(rdy, off_xd, sx) : 0.0f;
-        zv[i] = (GATE && ok) ? Elem<IO>::template load<kCached>(rz, off_xd, sx) : 0.0f;
         bv[i] = (ok && !FOLD) ? Elem<IO>::template load<0>(rb, off_bc, sb) : 0.0f;
         cv[i] = ok ? Elem<IO>::template load<0>(rc, off_bc, sb) : 0.0f;
       }
@@ -424,32 +446,57 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
     }
 
     // ---- pass 1 ----
-    float dl[K], fac[K], u[K], dyp[K], sg_z[K];
-    float sd = 0.0f;
+    float dl[K], fac[K], u[K], dyp[K], sg_z[K], xv[K], dyv[K], zv[K];
+    {
+      float dlo[KS], faco[KS], uo[KS], dypo[KS], sgo[KS];
 #pragma unroll
-    for (int i = 0; i < K; ++i) {
-      const bool ok = i < left;
-      const float raw = dlr[i] + dbias;
-      float v = raw, f = 1.0f;
-      if constexpr (SOFTPLUS) {
-        v = softplus_sigmoid_f32(raw, f);
+      for (int m = 0; m < KS; ++m) {
+        const bool ok = own_step(m) < left;
+        const float raw = dlr[m] + dbias;
+        float v = raw, f = 1.0f;
+        if constexpr (SOFTPLUS) {
+          v = softplus_sigmoid_f32(raw, f);
+        }
+        if constexpr (CLAMP) {
+          f = (v >= p.dmin && v <= p.dmax) ? f : 0.0f;
+          v = __builtin_amdgcn_fmed3f(v, p.dmin, p.dmax);
+        }
+        dlo[m] = ok ? v : 0.0f;
+        faco[m] = ok ? f : 0.0f;
+        uo[m] = dlo[m] * xo[m];
+        if constexpr (GATE) {
+          sgo[m] = sigmoid_f32(zo[m]);
+          dypo[m] = dyo[m] * zo[m] * sgo[m];
+        } else {
+          sgo[m] = 0.0f;
+          dypo[m] = dyo[m];
+        }
       }
-      if constexpr (CLAMP) {
-        f = (v >= p.dmin && v <= p.dmax) ? f : 0.0f;
-        v = __builtin_amdgcn_fmed3f(v, p.dmin, p.dmax);
-      }
-      dl[i] = ok ? v : 0.0f;
-      fac[i] = ok ? f : 0.0f;
-      u[i] = dl[i] * xv[i];
-      sd += dl[i];
+      share_rows(dlo, dl);
+      share_rows(faco, fac);
+      share_rows(uo, u);
+      share_rows(dypo, dyp);
+      if constexpr (!FOLD) share_rows(xo, xv);
       if constexpr (GATE) {
-        sg_z[i] = sigmoid_f32(zv[i]);
-        dyp[i] = dyv[i] * zv[i] * sg_z[i];
+        share_rows(sgo, sg_z);
+        share_rows(dyo, dyv);
+        share_rows(zo, zv);
       } else {
-        sg_z[i] = 0.0f;
-        dyp[i] = dyv[i];
+#pragma unroll
+        for (int i = 0; i < K; ++i) {
+          sg_z[i] = 0.0f;
+          dyv[i] = dyp[i];
+          zv[i] = 0.0f;
+        }
+      }
+      if constexpr (FOLD) {
+#pragma unroll
+        for (int i = 0; i < K; ++i) xv[i] = 0.0f;
       }
     }
+    float sd = 0.0f;
+#pragma unroll
+    for (int i = 0; i < K; ++i) sd += dl[i];
     // Abar and the input terms B u of both steps stay in registers for pass 2
     float ab[K][16], bu[K][16];
     float bt[16], mm[16];
