@@ -642,6 +642,25 @@ __global__ __launch_bounds__(64 * W, FOLD ? kFoldWavesPerSimd : kMinWavesPerSimd
     }  // serial walk
 
     // ---- pass 2: states from the incoming state, readout ----
+    // y of step i of the sub-chunk, summed over the state groups: the gate,
+    // the rounding and the store.  The step's offset from t_tile is soff_step
+    // in the scalar offset plus whatever voff adds to the lane's own row.
+    auto store_y = [&](int i, int soff_step, uint32_t voff, float yv0) __attribute__((always_inline)) {
+      const uint32_t sx = static_cast<uint32_t>((t_tile + soff_step) * xd_step);
+      if constexpr (GATE) {
+        // y * silu(z), silu(z) = z / (1 + 2^(-z log2 e)); padded steps never load z
+        const float zv = (FULL || i < left) ? Elem<IO>::template load<kCached>(rz, voff, sx) : 0.0f;
+        yv0 *= zv * __builtin_amdgcn_rcpf(1.0f + fast_exp2(-zv * kLog2e));
+      }
+      if constexpr (FULL) {
+        Elem<IO>::store(ry, voff, sx, yv0);
+      } else {
+        // the tile may run past L; only steps before L exist in y
+        const float yv = (i < left) ? yv0 : 0.0f;
+        if (i < L - t_tile - j * K) Elem<IO>::store(ry, voff, sx, yv);
+      }
+    };
+    float ysum[K];  // G > 1: this lane's partial y of each step (its 16 states)
 #pragma unroll
     for (int i = 0; i < K; ++i) {
       // A fresh name for B so that its broadcasts are not shared with pass 1
@@ -662,21 +681,41 @@ __global__ __launch_bounds__(64 * W, FOLD ? kFoldWavesPerSimd : kMinWavesPerSimd
           ya[3] = __builtin_fmaf(cq.w, h[s4 + 3], ya[3]);
         }
       }
-      float yv0 = sum_state_groups<G>((ya[0] + ya[1]) + (ya[2] + ya[3]));
-      if constexpr (GATE) {
-        // y * silu(z), silu(z) = z / (1 + 2^(-z log2 e)); padded steps never load z
-        const uint32_t sz = static_cast<uint32_t>((t_tile + i) * xd_step);
-        const float zv = (FULL || i < left) ? Elem<IO>::template load<kCached>(rz, off_xd, sz) : 0.0f;
-        yv0 *= zv * __builtin_amdgcn_rcpf(1.0f + fast_exp2(-zv * kLog2e));
+      ysum[i] = (ya[0] + ya[1]) + (ya[2] + ya[3]);
+      if constexpr (G == 1) store_y(i, i, off_xd, ysum[i]);
+    }
+    if constexpr (G > 1) {
+      // Reduce-scatter of the K partial sums over the G rows of the sub-chunk:
+      // row g ends with the total of steps g, g + G, .. (the steps it stores),
+      // added in the order (r0 + r1) + (r2 + r3).  v_permlane16_swap of the
+      // partials of steps 2m and 2m + 1 leaves the lower row of each pair
+      // holding both rows' step 2m and the upper row both rows' step 2m + 1;
+      // at G = 4, v_permlane32_swap then pairs the halves the same way.
+      float yown[KG];
+      auto swap_pair = [](float& a, float& b, bool halves) __attribute__((always_inline)) {
+        if (halves)
+          asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+        else
+          asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+      };
+      float pr[K / 2];
+#pragma unroll
+      for (int m = 0; m < K / 2; ++m) {
+        float a0 = ysum[2 * m], a1 = ysum[2 * m + 1];
+        swap_pair(a0, a1, false);
+        pr[m] = a0 + a1;
       }
-      const uint32_t sx = static_cast<uint32_t>((t_tile + i) * xd_step);
-      if constexpr (FULL) {
-        if (G == 1 || (i % G) == g) Elem<IO>::store(ry, off_xd, sx, yv0);
+      if constexpr (G == 2) {
+#pragma unroll
+        for (int m = 0; m < KG; ++m) yown[m] = pr[m];
       } else {
-        // the tile may run past L; only steps before L exist in y
-        const float yv = (i < left) ? yv0 : 0.0f;
-        if (i < L - t_tile - j * K && (G == 1 || (i % G) == g)) Elem<IO>::store(ry, off_xd, sx, yv);
+        float q0 = pr[0], q1 = pr[1];
+        swap_pair(q0, q1, true);
+        yown[0] = q0 + q1;
       }
+      const uint32_t off_own = off_xd + static_cast<uint32_t>(g * nd * E);
+#pragma unroll
+      for (int m = 0; m < KG; ++m) store_y(g + G * m, G * m, off_own, yown[m]);
     }
     if constexpr (WSCAN && !FOLD) {
       // chunk-boundary states: the state after a sub-chunk that ends a chunk
