@@ -608,6 +608,35 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
 #pragma unroll
     for (int s = 0; s < 16; ++s) hm[s] = __builtin_fmaf(ab[0][s], hp[s], bu[0][s]);
 
+    // The per-(step, channel) results of step i from the sums over all states
+    // (sgb = sum_n g B, sda = sum_n g h Abar A, ypre = C.h for the gate):
+    // dx, ddelta_raw, dz, and the dD and dbias accumulators.  The step's
+    // offset from t_tile is soff_step in the scalar offset plus whatever voff
+    // adds to the lane's own row.
+    auto step_out = [&](int i, float sgb, float sda, float ypre, uint32_t voff, int soff_step)
+                        __attribute__((always_inline)) {
+      const float xi = xv[i], yi = dyp[i];
+      if constexpr (GATE) ypre += dskip * xi;
+      const float ddt = __builtin_fmaf(xi, sgb, sda * kLn2);  // A = A2 ln 2
+      const float ddraw = ddt * fac[i];
+      const float dxv = __builtin_fmaf(dl[i], sgb, yi * dskip);
+      const uint32_t sx = static_cast<uint32_t>((t_tile + soff_step) * xd_step);
+      if ((full || i < left) && (G == 1 || (i % G) == g)) {
+        Elem<IO>::store(rdx, voff, sx, dxv);
+        Elem<IO>::store(rdd, voff, sx, ddraw);
+        if constexpr (GATE) {
+          const float sz = sg_z[i];
+          Elem<IO>::store(rdz, voff, sx, dyv[i] * ypre * sz * __builtin_fmaf(zv[i], 1.0f - sz, 1.0f));
+        }
+        dD_acc = __builtin_fmaf(yi, xi, dD_acc);
+        db_acc += ddraw;
+      } else if (j * K + i < L - t_tile && (G == 1 || (i % G) == g)) {
+        Elem<IO>::store(rdx, voff, sx, 0.0f);
+        Elem<IO>::store(rdd, voff, sx, 0.0f);
+        if constexpr (GATE) Elem<IO>::store(rdz, voff, sx, 0.0f);
+      }
+    };
+    float sg_p[K], sda_p[K], yp_p[K];  // G > 1: this lane's partial sums of each step (its 16 states)
 #pragma unroll
     for (int ii = 0; ii < K; ++ii) {
       const int i = K - 1 - ii;  // steps in reverse
@@ -653,28 +682,32 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
         wdB[t * N + 16 * g + c] = sB;
         wdC[t * N + 16 * g + c] = sC;
       }
-      const float sgb = sum_state_groups<G>((sg4[0] + sg4[1]) + (sg4[2] + sg4[3]));
-      const float sda = sum_state_groups<G>((sda4[0] + sda4[1]) + (sda4[2] + sda4[3]));
-      if constexpr (GATE) ypre = sum_state_groups<G>(ypre) + dskip * xv[i];
-      const float ddt = __builtin_fmaf(xv[i], sgb, sda * kLn2);  // A = A2 ln 2
-      const float ddraw = ddt * fac[i];
-      const float dxv = __builtin_fmaf(dl[i], sgb, yi * dskip);
-      if ((full || i < left) && (G == 1 || (i % G) == g)) {
-        const uint32_t sx = static_cast<uint32_t>((t_tile + i) * xd_step);
-        Elem<IO>::store(rdx, off_xd, sx, dxv);
-        Elem<IO>::store(rdd, off_xd, sx, ddraw);
-        if constexpr (GATE) {
-          const float sz = sg_z[i];
-          Elem<IO>::store(rdz, off_xd, sx, dyv[i] * ypre * sz * __builtin_fmaf(zv[i], 1.0f - sz, 1.0f));
+      sg_p[i] = (sg4[0] + sg4[1]) + (sg4[2] + sg4[3]);
+      sda_p[i] = (sda4[0] + sda4[1]) + (sda4[2] + sda4[3]);
+      yp_p[i] = ypre;
+      if constexpr (G == 1) step_out(i, sg_p[i], sda_p[i], ypre, off_xd, i);
+    }
+    if constexpr (G > 1) {
+      // Reduce-scatter of the two steps' partial sums over the state-group
+      // rows, in the order (r0 + r1) + (r2 + r3): v_permlane16_swap of the
+      // partials of steps 0 and 1 leaves row 2q (2q + 1) of each pair with
+      // both rows' step 0 (1); at G = 4 v_permlane32_swap then adds the two
+      // halves.  Row r ends with the totals of step r % 2, the step it
+      // discretised and (rows g < 2 at G = 4) stores.
+      auto scatter = [](float v0, float v1) __attribute__((always_inline)) {
+        asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(v0), "+v"(v1));
+        float t = v0 + v1;
+        if constexpr (G == 4) {
+          float lo, hi;
+          rows_swap32(t, lo, hi);
+          t = lo + hi;
         }
-        dD_acc = __builtin_fmaf(yi, xv[i], dD_acc);
-        db_acc += ddraw;
-      } else if (j * K + i < L - t_tile && (G == 1 || (i % G) == g)) {
-        const uint32_t sx = static_cast<uint32_t>((t_tile + i) * xd_step);
-        Elem<IO>::store(rdx, off_xd, sx, 0.0f);
-        Elem<IO>::store(rdd, off_xd, sx, 0.0f);
-        if constexpr (GATE) Elem<IO>::store(rdz, off_xd, sx, 0.0f);
-      }
+        return t;
+      };
+      const float sgb = scatter(sg_p[0], sg_p[1]);
+      const float sda = scatter(sda_p[0], sda_p[1]);
+      const float ypre = GATE ? scatter(yp_p[0], yp_p[1]) : 0.0f;
+      step_out(r & 1, sgb, sda, ypre, off_xd_own, 0);
     }
   }
 
