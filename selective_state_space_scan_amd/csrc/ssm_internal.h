@@ -126,31 +126,6 @@ __device__ __forceinline__ void dot16_row_bcast(float (&y)[4], float c, const fl
         "v"(h[8]), "v"(h[9]), "v"(h[10]), "v"(h[11]), "v"(h[12]), "v"(h[13]), "v"(h[14]), "v"(h[15]));
 }
 
-// Sum of v over the G state-group rows that share a time sub-chunk; every lane
-// of those rows gets the same bits (fixed order: (r0 + r1) + (r2 + r3)).
-// v_permlane16_swap exchanges rows 0<->1 and 2<->3 between its two operands,
-// v_permlane32_swap the two 32-lane halves; starting both operands from the
-// same value leaves each lane with its own value and its partner's.  Written
-// out because the compiler folds the builtin's two results into one when both
-// operands are the same value.  s_nop 1 covers the VALU-write -> permlane-read
-// hazard.
-template <int G>
-__device__ __forceinline__ float sum_state_groups(float v) {
-  if constexpr (G == 1) {
-    return v;
-  } else {
-    float a = v, b = v;
-    asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
-    float s = a + b;
-    if constexpr (G == 4) {
-      float c = s, d = s;
-      asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(c), "+v"(d));
-      s = c + d;
-    }
-    return s;
-  }
-}
-
 // Row exchanges between the four 16-lane rows of a wave.  With both operands
 // v, v_permlane16_swap leaves the rows [0, 0, 2, 2] of v in the first operand
 // and [1, 1, 3, 3] in the second; v_permlane32_swap leaves [0, 1, 0, 1] and

@@ -37,7 +37,8 @@
 //    branch), and y = +0 there.  Tiles that lie wholly in the padding are not
 //    loaded at all.
 //  * With G > 1 the 16-state partial sums of y from the G state-group rows are
-//    added with v_permlane16_swap / v_permlane32_swap in a fixed order.
+//    reduce-scattered with v_permlane16_swap / v_permlane32_swap in a fixed
+//    order, so that each row holds the totals of the steps it stores.
 //  * The carry walk can be replaced by a log-depth (Hillis-Steele) scan across
 //    each wave's sub-chunks with a walk over the wave totals only
 //    (extras.combine; slower on this GPU, kept as an option).
