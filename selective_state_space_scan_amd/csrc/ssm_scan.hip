@@ -743,8 +743,10 @@ __global__ __launch_bounds__(64 * W, FOLD ? kFoldWavesPerSimd : kMinWavesPerSimd
   // the current tile (1 % faster than loading them at its top).  At 32 and 64
   // the registers they occupy across the tile made the compiler spill (24 and
   // 80 bytes per lane); there each tile loads its own at its top: 1 % and 2 %
-  // faster (the fold kernel too, though it does not spill either way).
-  constexpr bool kPrefetch = G == 1;
+  // faster (the fold kernel too, though it does not spill either way).  The
+  // wave-scan combine, which needs more registers, never prefetches (dstate
+  // 16: 108 -> 56 bytes spilled, 16 % faster).
+  constexpr bool kPrefetch = G == 1 && !WSCAN;
   const int64_t nfull = len / T;
   uint32_t xa[KG], da[KG], xn[KG], dn[KG];
   if (kPrefetch && nfull > 0) load_xd.template operator()<true>(0, xa, da);
