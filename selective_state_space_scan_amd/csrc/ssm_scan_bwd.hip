@@ -95,6 +95,10 @@ struct BwdParams {
 };
 
 constexpr int kBwdK = 2;  // steps per lane and sub-chunk
+// The fold kernel of a time split keeps no per-step state (no Abar cache, no
+// pass 2), so its sub-chunks are longer: the walk's exp and FMA chain per
+// (pair, sub-chunk) is then spread over 8 steps instead of 2.
+constexpr int kBwdFoldK = 8;
 // Waves per workgroup: 4 when the grid fills the GPU (two workgroups share a
 // CU and cover each other's barriers), 8 for small grids (more waves per
 // (row, channel group)).  The chunk length of the saved states is the 4-wave
@@ -198,8 +202,8 @@ __device__ __forceinline__ float row_reduce_scatter16(const float (&v)[16], int 
 // over parts 1 .. n_parts-1).  Otherwise the backward over every part.
 template <typename IO, int G, int W, bool SOFTPLUS, bool CLAMP, bool GATE, bool FOLD>
 __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
-  constexpr int K = kBwdK;
-  constexpr int CS = W / kBwdW;  // saved chunks per tile
+  constexpr int K = FOLD ? kBwdFoldK : kBwdK;
+  constexpr int CS = W / kBwdW;  // saved chunks per tile (not used by the fold)
   constexpr int N = 16 * G;
   constexpr int QR = 4 / G;
   constexpr int SUB = W * QR;  // sub-chunks per tile
@@ -330,20 +334,34 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
   const rsrc_t rc = make_rsrc(static_cast<const char*>(p.C) + bc_base, bc_row);
   const uint32_t off_xd = static_cast<uint32_t>((j * K * nd + d) * E);
   // The 2 (dstate 32) or 4 (dstate 64) state-group rows of a sub-chunk share
-  // its K = 2 steps: a lane loads x, delta, dy, z and runs softplus, the clip
-  // and the gate only for its own step (row r takes step r % 2), and the rows
-  // exchange the results with v_permlane16_swap (rows [0, 0, 2, 2] hold step
-  // 0 afterwards, rows [1, 1, 3, 3] step 1).  At dstate 16 a lane has both.
-  constexpr int KS = G == 1 ? K : 1;  // steps a lane discretises
-  static_assert(K == 2, "the row exchange pairs rows 2q and 2q + 1 over two steps");
-  auto own_step = [&](int m) { return G == 1 ? m : (r & 1); };
-  const uint32_t off_xd_own = off_xd + static_cast<uint32_t>(G == 1 ? 0 : (r & 1) * nd * E);
+  // its steps: a lane loads x, delta, dy, z and runs softplus, the clip and
+  // the gate only for its own steps, and the rows exchange the results with
+  // v_permlane16_swap (and v_permlane32_swap).  With K = 2 steps row r takes
+  // step r % 2 (rows [0, 0, 2, 2] hold step 0 after the swap, rows
+  // [1, 1, 3, 3] step 1); in the fold (K = 8) row g takes steps g*KS ..
+  // g*KS + KS-1.  At dstate 16 a lane has all its steps.
+  constexpr int KS = G == 1 ? K : (FOLD ? K / G : 1);  // steps a lane discretises
+  static_assert(FOLD || K == 2, "the row exchange pairs rows 2q and 2q + 1 over two steps");
+  static_assert(!FOLD || K % G == 0, "the fold's rows split a sub-chunk's steps evenly");
+  auto own_step = [&](int m) { return G == 1 ? m : (FOLD ? g * KS + m : (r & 1)); };
+  const uint32_t off_xd_own = off_xd + static_cast<uint32_t>((G == 1 ? 0 : (FOLD ? g * KS : (r & 1))) * nd * E);
   auto share_rows = [](const float (&own)[KS], float (&all)[K]) __attribute__((always_inline)) {
     if constexpr (G == 1) {
 #pragma unroll
       for (int i = 0; i < K; ++i) all[i] = own[i];
-    } else {
+    } else if constexpr (!FOLD) {
       rows_swap16(own[0], all[0], all[1]);
+    } else if constexpr (G == 2) {
+#pragma unroll
+      for (int m = 0; m < KS; ++m) rows_swap16(own[m], all[m], all[KS + m]);  // rows 2q and 2q + 1
+    } else {
+#pragma unroll
+      for (int m = 0; m < KS; ++m) {
+        float lo, hi;
+        rows_swap16(own[m], lo, hi);  // rows [0, 0, 2, 2] and [1, 1, 3, 3]
+        rows_swap32(lo, all[m], all[2 * KS + m]);
+        rows_swap32(hi, all[KS + m], all[3 * KS + m]);
+      }
     }
   };
   const uint32_t off_bc = static_cast<uint32_t>((j * K * N + 16 * g + c) * E);
@@ -498,24 +516,39 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < K; ++i) sd += dl[i];
     // Abar and the input terms B u of both steps stay in registers for pass 2
+    // (the fold kernel, which has no pass 2, leaves ab, bu and cy unused)
     float ab[K][16], bu[K][16];
     float bt[16], mm[16];
+    // c = dyp C (pass 2 adds the same terms to the adjoint)
+    float cy[K][16];
+    if constexpr (FOLD) {
+      // the sub-chunk's reverse fold from zero, m = Abar_0 (c_0 + Abar_1 (c_1
+      // + .. Abar_{K-1} c_{K-1})), from the last step back with one FMA per
+      // step: p = c_{K-1}, p = Abar_i p + c_{i-1}, m = Abar_0 p
+      float pp[16];
+      {
+        const float ck = cv[K - 1], yk = dyp[K - 1];
+        Unroll<0, 16>::run([&]<int S>() { pp[S] = row_bcast<S>(ck) * yk; });
+      }
 #pragma unroll
-    for (int i = 0; i < K; ++i) {
-      const float bi = bv[i];
-      const float ui = u[i];
-      Unroll<0, 16>::run([&]<int S>() {
-        ab[i][S] = fast_exp2(dl[i] * A2[S]);
-        if constexpr (!FOLD) {
+      for (int i = K - 1; i >= 1; --i) {
+        const float cp = cv[i - 1], yp = dyp[i - 1], dli = dl[i];
+        Unroll<0, 16>::run(
+            [&]<int S>() { pp[S] = __builtin_fmaf(fast_exp2(dli * A2[S]), pp[S], row_bcast<S>(cp) * yp); });
+      }
+      Unroll<0, 16>::run([&]<int S>() { mm[S] = fast_exp2(dl[0] * A2[S]) * pp[S]; });
+    } else {
+#pragma unroll
+      for (int i = 0; i < K; ++i) {
+        const float bi = bv[i];
+        const float ui = u[i];
+        Unroll<0, 16>::run([&]<int S>() {
+          ab[i][S] = fast_exp2(dl[i] * A2[S]);
           bu[i][S] = row_bcast<S>(bi) * ui;
           bt[S] = (i == 0) ? bu[0][S] : __builtin_fmaf(ab[i][S], bt[S], bu[i][S]);
-        }
-      });
-    }
-    // reverse fold over the K = 2 steps: m = Abar_0 (c_0 + Abar_1 c_1) with
-    // c = dyp C; pass 2 adds the same c terms to the adjoint
-    float cy[K][16];
-    {
+        });
+      }
+      // the reverse fold over the K = 2 steps: m = Abar_0 (c_0 + Abar_1 c_1)
       const float c0 = cv[0], c1 = cv[1], y0 = dyp[0], y1 = dyp[1];
       Unroll<0, 16>::run([&]<int S>() {
         cy[0][S] = row_bcast<S>(c0) * y0;
