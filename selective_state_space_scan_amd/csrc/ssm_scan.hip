@@ -331,8 +331,8 @@ __global__ __launch_bounds__(64 * W, FOLD ? kFoldWavesPerSimd : kMinWavesPerSimd
   };
   // The values of all K steps of the sub-chunk from the rows that computed
   // them (own: this lane's KG steps): at G = 2 the row pair exchanges through
-  // v_permlane16_swap; at G = 4 each row holds one step and the four are
-  // gathered with one v_permlane16_swap and two v_permlane32_swap.
+  // v_permlane16_swap; at G = 4 each of the four rows' steps are gathered with
+  // one v_permlane16_swap and two v_permlane32_swap.
   auto share_rows = [](const float (&own)[KG], float (&all)[K]) __attribute__((always_inline)) {
     if constexpr (G == 1) {
 #pragma unroll
@@ -341,10 +341,13 @@ __global__ __launch_bounds__(64 * W, FOLD ? kFoldWavesPerSimd : kMinWavesPerSimd
 #pragma unroll
       for (int m = 0; m < KG; ++m) rows_swap16(own[m], all[m], all[KG + m]);  // rows 2q and 2q+1
     } else {
-      float lo, hi;
-      rows_swap16(own[0], lo, hi);   // rows [0, 0, 2, 2] and [1, 1, 3, 3]
-      rows_swap32(lo, all[0], all[2]);
-      rows_swap32(hi, all[1], all[3]);
+#pragma unroll
+      for (int m = 0; m < KG; ++m) {
+        float lo, hi;
+        rows_swap16(own[m], lo, hi);  // rows [0, 0, 2, 2] and [1, 1, 3, 3]
+        rows_swap32(lo, all[m], all[2 * KG + m]);
+        rows_swap32(hi, all[KG + m], all[3 * KG + m]);
+      }
     }
   };
 
@@ -685,7 +688,7 @@ __global__ __launch_bounds__(64 * W, FOLD ? kFoldWavesPerSimd : kMinWavesPerSimd
       ysum[i] = (ya[0] + ya[1]) + (ya[2] + ya[3]);
       if constexpr (G == 1) store_y(i, i, off_xd, ysum[i]);
     }
-    if constexpr (G > 1) {
+    if constexpr (G > 1 && !FOLD) {  // (the fold kernel has returned above)
       // Reduce-scatter of the K partial sums over the G rows of the sub-chunk:
       // row g ends with the total of steps g, g + G, .. (the steps it stores),
       // added in the order (r0 + r1) + (r2 + r3).  v_permlane16_swap of the
