@@ -279,9 +279,9 @@ typedef struct ssm_scan_bwd_io {
 int64_t ssm_scan_bwd_chunk_len(int64_t dstate);
 
 /* Workspace bytes of ssm_selective_scan_bwd for these dims: 4 * (2 * (dim/16)
- * * batch * seqlen * dstate + 15 * batch * dim * dstate + 23 * batch * dim)
+ * * batch * seqlen * dstate + 31 * batch * dim * dstate + 47 * batch * dim)
  * (dB/dC partials per channel group, and per-part partials for a time split
- * into up to 8 parts, which the library uses when the batch is too small to
+ * into up to 16 parts, which the library uses when the batch is too small to
  * fill the GPU); -1 for NULL or invalid dims. */
 int64_t ssm_scan_bwd_workspace_bytes(const ssm_scan_dims* dims);
 

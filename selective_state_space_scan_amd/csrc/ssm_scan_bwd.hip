@@ -933,7 +933,7 @@ hipError_t bwd_launch_io(int G, const BwdParams& prm, bool sp, bool wide, hipStr
   }
 }
 
-constexpr int64_t kBwdMaxParts = 8;
+constexpr int64_t kBwdMaxParts = 16;
 
 // Workspace floats: dB and dC partials per channel group; dA, dD and dbias per
 // (part, row); the fold's adjoint and delta sums per (part >= 1, row) -- sized
@@ -1063,10 +1063,14 @@ int ssm_selective_scan_bwd(ssm_scan_t handle, const void* x, const void* delta, 
   prm.dh0 = io->dh0;
   // Time split: while the (row, channel group) grid would leave CUs idle (at
   // most two thirds as many groups as CUs), cut time into parts of whole
-  // tiles (at most 8, at least four tiles per part).  Above that the split
-  // costs more than it balances (measured at 4096 steps: 192 groups 3 / 6 /
-  // 8 % slower split at dstate 16 / 32 / 64; dstate 16, 256 groups 0.369 ms
-  // split, 0.338 ms not; 448 groups 0.678 / 0.570 ms).
+  // tiles: about two workgroups per resident slot, at most 16 parts and at
+  // least four tiles per part.  Above that the split costs more than it
+  // balances (measured at 4096 steps: 192 groups 3 / 6 / 8 % slower split at
+  // dstate 16 / 32 / 64; dstate 16, 256 groups 0.369 ms split, 0.338 ms not;
+  // 448 groups 0.678 / 0.570 ms).  With few groups the cap matters: 32 groups
+  // of 16384 steps 0.258 ms in 8 parts, 0.190 ms in 16; at 128 groups 16
+  // parts lost 1-4 % against the 8 this rule gives (except 2 % gained on
+  // 32768 steps).
   const int64_t groups = nb * n_cg;
   const int64_t slots = 2 * static_cast<int64_t>(handle->cu_count);
   int64_t parts = 1, part_len = L;

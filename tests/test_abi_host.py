@@ -248,7 +248,7 @@ def test_bwd_checks():
     assert ssm.bwd_chunk_len(8) == 0
     d = _dims(batch=2, seqlen=100, dim=32, dstate=16)
     need = ssm.bwd_workspace_bytes(d)
-    assert need == 4 * (2 * 2 * 2 * 100 * 16 + 15 * 2 * 32 * 16 + 23 * 2 * 32)
+    assert need == 4 * (2 * 2 * 2 * 100 * 16 + 31 * 2 * 32 * 16 + 47 * 2 * 32)
     assert ssm.bwd_workspace_bytes(_dims(dstate=8)) == -1 and ssm.bwd_workspace_bytes(_dims(dim=24)) == -1
 
     def io(**kw):
