@@ -118,6 +118,18 @@ def test_bwd_deterministic():
             assert np.array_equal(a[k].cpu().float().numpy(), b[k].cpu().float().numpy()), k
 
 
+@pytest.mark.parametrize("io,N", [("f32", 16), ("f32", 32), ("f32", 64), ("bf16", 64)])
+def test_bwd_many_parts_ragged(io, N):
+    """Two rows of 32 channels leave the GPU idle, so the backward splits time
+    into nine parts of five tiles, folded over 8-step sub-chunks; the second
+    row ends inside the fifth part (a ragged fold) and is padding after it."""
+    import selective_state_space_scan_amd as ssm
+    T = ssm.bwd_chunk_len(N)
+    L = 40 * T + 11
+    w, inp = _case(io, N, L, 2, 32, seed=500 + N, varlen=[L, 23 * T + 7])
+    _compare(_gpu(inp, io), _oracle(inp), io, f"{io} N={N} nine parts")
+
+
 def test_bwd_after_time_split_forward():
     """The chunk states of a time-split forward serve the backward equally."""
     w, inp = _case("bf16", 64, 2048, 1, 32, seed=13)
