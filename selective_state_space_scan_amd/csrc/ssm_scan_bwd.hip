@@ -35,8 +35,13 @@
 //    contributions to dB and dC are summed over the 16 channels by a DPP
 //    reduce-scatter across the lanes and written as one partial per channel
 //    group.
-// A second kernel sums the partials over channel groups (dB, dC) and over
-// batch rows (dA_log, dD, dbias) in a fixed order, so the result is
+// At dstate 32 and 64 the state-group rows of a sub-chunk split its
+// per-(step, channel) work (loads, softplus, gate) and reduce-scatter their
+// per-step sums over states, exchanging values with v_permlane16/32_swap.
+// With a time split, a fold kernel first folds the adjoint of every part but
+// the first from zero, over 8-step sub-chunks (it keeps no per-step state).
+// A last kernel sums the partials over channel groups (dB, dC) and over
+// batch rows and parts (dA_log, dD, dbias) in a fixed order, so the result is
 // deterministic.
 //
 // All arithmetic is fp32.
