@@ -131,6 +131,43 @@ def kernel_percentiles(kern_ms) -> dict:
             "kernel_ms_p90": round(float(p[2]), 5)}
 
 
+TIMING_NOTES = {
+    "kernel_avg_ms_from": "the timed region: K launches back to back between one pair of HIP events",
+    "kernel_ms_percentiles_from": "a separate pass of K launches after the timed region, each between its own events",
+}
+
+
+def time_steps(step, steps: int, stream) -> float:
+    """The timed region: `steps` launches back to back on `stream`, between one
+    pair of HIP events, bracketed by synchronisations; ms per step.  No event
+    is recorded between the launches: an event between two launches of the
+    forward made the second one ~5 % slower on this GPU, so the per-launch
+    average is the region's time over the launches (inter-launch gaps
+    included)."""
+    import torch
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for k in range(steps):
+        step(k)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    return t_start.elapsed_time(t_end) / steps
+
+
+def per_launch_ms(step, steps: int, stream) -> list:
+    """After the timed region, untimed: `steps` more launches, each between its
+    own pair of events, for the spread of single launch times (ms)."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for k in range(steps):
+        ev[k][0].record(stream)
+        step(k)
+        ev[k][1].record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
 def host_cpu() -> dict:
     """The host the CPU baseline ran on: processor model, logical CPUs, and
     the CPUs this process may use."""
@@ -356,20 +393,9 @@ def main() -> int:
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for k in range(args.steps):
-        ev[k][0].record(stream)
-        step(k)
-        ev[k][1].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    kern_ms = [a.elapsed_time(b) for a, b in ev]
-    ms_per_step = total_ms / args.steps
-    kern_avg_ms = float(np.mean(kern_ms))
+    ms_per_step = time_steps(step, args.steps, stream)
+    kern_avg_ms = ms_per_step
+    kern_ms = per_launch_ms(step, args.steps, stream)
 
     steps_valid = w.batch * w.seqlen if inp["valid_len"] is None else int(np.sum(inp["valid_len"]))
     updates = steps_valid * w.dim * w.dstate
@@ -391,6 +417,7 @@ def main() -> int:
                       f"ssm_fwd_kernel: fold of {parts - 1} time parts, then the forward over {parts} parts")
     roof["kernel_avg_ms"] = round(kern_avg_ms, 5)
     roof.update(kernel_percentiles(kern_ms))
+    roof.update(TIMING_NOTES)
     roof["hbm_gbps"] = round(gbps, 1)
     roof["hbm_frac"] = round(gbps / HBM_PEAK_GBPS, 4)
     roof["algorithmic_bytes"] = nbytes
@@ -489,19 +516,9 @@ def bench_bwd(args, w, inp) -> int:
         step(k)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for k in range(args.steps):
-        ev[k][0].record(stream)
-        step(k)
-        ev[k][1].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    ms_per_step = t_start.elapsed_time(t_end) / args.steps
-    kern_ms = [a.elapsed_time(b) for a, b in ev]
-    kern_avg_ms = float(np.mean(kern_ms))
+    ms_per_step = time_steps(step, args.steps, stream)
+    kern_avg_ms = ms_per_step
+    kern_ms = per_launch_ms(step, args.steps, stream)
     steps_valid = w.batch * w.seqlen if inp["valid_len"] is None else int(np.sum(inp["valid_len"]))
     updates = steps_valid * w.dim * w.dstate
     e = 2 if w.io == "bf16" else 4
@@ -520,6 +537,7 @@ def bench_bwd(args, w, inp) -> int:
                  "hbm_gbps": round(gbps, 1), "hbm_frac": round(gbps / HBM_PEAK_GBPS, 4), "algorithmic_bytes": nbytes,
                  "algorithmic_tflop": flops / 1e12, "traffic_unit": "bytes per launch"})
     roof.update(kernel_percentiles(kern_ms))
+    roof.update(TIMING_NOTES)
     peaks = None if args.no_peaks else measure_peaks(dev)
     if peaks is not None:
         add_measured_peak(roof, peaks)
