@@ -247,9 +247,9 @@ def test_bwd_binding_rejects_bad_arguments():
 
 
 def test_bwd_outputs_only_4_byte_aligned():
-    """dB and dC only 4-byte (not 16-byte) aligned, through the raw entry point:
-    the same bits as the binding's call with its own (aligned) outputs."""
-    import ctypes
+    """dB and dC, or the workspace, only 4-byte (not 16-byte) aligned, through
+    the raw entry point: the same bits as the binding's call with its own
+    (aligned) buffers."""
     import torch
     import selective_state_space_scan_amd as ssm
     w, inp = _case("bf16", 16, 300, 2, 32, seed=91, varlen=[300, 177], extras=False)
@@ -267,25 +267,27 @@ def test_bwd_outputs_only_4_byte_aligned():
     dims = ssm.ssm_scan_dims()
     dims.batch, dims.seqlen, dims.dim, dims.dstate = nb, L, nd, 16
     dims.io_dtype, dims.delta_softplus = ssm.SSM_IO_BF16, 1
-    big = torch.full((2 * n + 8,), float("nan"), dtype=torch.float32, device="cuda")
-    dB, dC = big[1:1 + n], big[n + 2:2 * n + 2]  # 4 and 8 bytes past a 256-byte boundary
-    out = {k: torch.empty_like(v) for k, v in ref.items() if v is not None and k not in ("dB", "dC")}
     nbytes = ssm.bwd_workspace_bytes(dims)
-    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     p = lambda t: None if t is None else t.data_ptr()
-    bio = ssm.ssm_scan_bwd_io(p(dy), p(dhl), p(cs), p(out["dx"]), p(out["ddelta"]), None, p(out["dA_log"]),
-                              p(dB), p(dC), p(out["dD"]), None, p(out["dh0"]), p(ws), nbytes)
     h = ssm._binding.handle_for(torch.cuda.current_device())
-    rc = ssm.ssm_selective_scan_bwd(h, p(dev["x"]), p(dev["delta"]), p(dev["A_log"]), p(dev["B"]), p(dev["C"]),
-                                    p(dev["D"]), p(dev["valid_len"]), dims, None, bio,
-                                    torch.cuda.current_stream().cuda_stream)
-    assert rc == ssm.SSM_OK
-    torch.cuda.synchronize()
-    for k, got in (("dB", dB), ("dC", dC), ("dx", out["dx"]), ("dA_log", out["dA_log"])):
-        bits = torch.int16 if got.dtype == torch.bfloat16 else torch.int32
-        a = got.contiguous().view(bits).reshape(-1).cpu().numpy()
-        b = ref[k].contiguous().view(bits).reshape(-1).cpu().numpy()
-        assert np.array_equal(a, b), k
+    for outs_off, ws_off in ((1, 0), (0, 4)):
+        big = torch.full((2 * n + 8,), float("nan"), dtype=torch.float32, device="cuda")
+        # dB 4 bytes and dC 8 bytes past a 256-byte boundary, or both aligned
+        dB, dC = (big[1:1 + n], big[n + 2:2 * n + 2]) if outs_off else (big[:n], big[n + 4:2 * n + 4])
+        out = {k: torch.empty_like(v) for k, v in ref.items() if v is not None and k not in ("dB", "dC")}
+        ws = torch.empty(nbytes + 16, dtype=torch.uint8, device="cuda")[ws_off:ws_off + nbytes]
+        bio = ssm.ssm_scan_bwd_io(p(dy), p(dhl), p(cs), p(out["dx"]), p(out["ddelta"]), None, p(out["dA_log"]),
+                                  p(dB), p(dC), p(out["dD"]), None, p(out["dh0"]), p(ws), nbytes)
+        rc = ssm.ssm_selective_scan_bwd(h, p(dev["x"]), p(dev["delta"]), p(dev["A_log"]), p(dev["B"]), p(dev["C"]),
+                                        p(dev["D"]), p(dev["valid_len"]), dims, None, bio,
+                                        torch.cuda.current_stream().cuda_stream)
+        assert rc == ssm.SSM_OK
+        torch.cuda.synchronize()
+        for k, got in (("dB", dB), ("dC", dC), ("dx", out["dx"]), ("dA_log", out["dA_log"])):
+            bits = torch.int16 if got.dtype == torch.bfloat16 else torch.int32
+            a = got.contiguous().view(bits).reshape(-1).cpu().numpy()
+            b = ref[k].contiguous().view(bits).reshape(-1).cpu().numpy()
+            assert np.array_equal(a, b), (k, outs_off, ws_off)
 
 
 def test_bwd_length_paired_rows_bit_exact():
