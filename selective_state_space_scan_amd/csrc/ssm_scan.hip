@@ -560,7 +560,7 @@ __global__ __launch_bounds__(64 * W, FOLD ? kFoldWavesPerSimd : kMinWavesPerSimd
     float cb_last = 0.0f;
     if constexpr (G == 1 && !FOLD && !WSCAN) {
       auto dpp = []<int CTRL>(float v) {
-        return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+        return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xf, 0xf, true));
       };
       float t = bv[K - 1] * cv[K - 1];
       t += dpp.template operator()<0xb1>(t);   // quad_perm [1, 0, 3, 2]
@@ -692,7 +692,7 @@ __global__ __launch_bounds__(64 * W, FOLD ? kFoldWavesPerSimd : kMinWavesPerSimd
       float bi = bv[i];
       asm volatile("" : "+v"(bi));
       const float ui = u[i];
-      float ya[4] = {dskip * xv[i], 0.0f, 0.0f, 0.0f};
+      float ya[2] = {dskip * xv[i], 0.0f};  // two chains: one add per step to join them
       if (G == 1 && !WSCAN && i == K - 1) {
         // the last step: Abar h only, its B u term as u (C . B) (see pass 1)
         Unroll<0, 16>::run([&]<int S>() { h[S] = ab[i][S] * h[S]; });
@@ -707,11 +707,11 @@ __global__ __launch_bounds__(64 * W, FOLD ? kFoldWavesPerSimd : kMinWavesPerSimd
           const float4 cq = *reinterpret_cast<const float4*>(crow + s4);
           ya[0] = __builtin_fmaf(cq.x, h[s4], ya[0]);
           ya[1] = __builtin_fmaf(cq.y, h[s4 + 1], ya[1]);
-          ya[2] = __builtin_fmaf(cq.z, h[s4 + 2], ya[2]);
-          ya[3] = __builtin_fmaf(cq.w, h[s4 + 3], ya[3]);
+          ya[0] = __builtin_fmaf(cq.z, h[s4 + 2], ya[0]);
+          ya[1] = __builtin_fmaf(cq.w, h[s4 + 3], ya[1]);
         }
       }
-      ysum[i] = (ya[0] + ya[1]) + (ya[2] + ya[3]);
+      ysum[i] = ya[0] + ya[1];
       if constexpr (G == 1) store_y(i, i, off_xd, ysum[i]);
     }
     if constexpr (G > 1 && !FOLD) {  // (the fold kernel has returned above)
