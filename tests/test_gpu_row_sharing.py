@@ -3,10 +3,12 @@ one time sub-chunk share its per-(step, channel) work: each row loads x and
 delta and runs softplus, the clip and the gate for some of the sub-chunk's
 steps and the rows exchange the results; the readout sums (forward) and the
 sums over states (backward) are reduce-scattered so that each row finishes the
-steps it stores.  Rows whose valid length ends at every step of a sub-chunk
-put the boundary between the rows' steps in every position; forward and
-backward are checked against the fp64 oracle, with the gate, h0, a delta bias,
-the clip and chunk-boundary states."""
+steps it stores.  At dstate 16 the forward reads out each sub-chunk's last
+step as C.(Abar h) + u (C.B).  Rows whose valid length ends at every step of
+a sub-chunk put the boundary between the rows' steps, and the sub-chunk's
+last step, in every position; forward and backward are checked against the
+fp64 oracle, with the gate, h0, a delta bias, the clip and chunk-boundary
+states."""
 import numpy as np
 import pytest
 
@@ -24,7 +26,7 @@ def _lengths(T):
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-@pytest.mark.parametrize("N", [32, 64])
+@pytest.mark.parametrize("N", [16, 32, 64])
 def test_forward_lengths_ending_at_every_step_of_a_sub_chunk(io, N):
     import torch
     import selective_state_space_scan_amd as ssm
@@ -51,7 +53,7 @@ def test_forward_lengths_ending_at_every_step_of_a_sub_chunk(io, N):
 
 
 @pytest.mark.parametrize("io", ["f32", "bf16"])
-@pytest.mark.parametrize("N", [32, 64])
+@pytest.mark.parametrize("N", [16, 32, 64])
 def test_backward_lengths_ending_at_every_step_of_a_sub_chunk(io, N):
     import selective_state_space_scan_amd as ssm
     T = ssm.bwd_chunk_len(N)
