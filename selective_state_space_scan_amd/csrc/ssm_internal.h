@@ -75,18 +75,22 @@ struct Elem<uint16_t> {
 
 __device__ __forceinline__ float fast_exp2(float v) { return __builtin_amdgcn_exp2f(v); }
 
-// softplus(v) = max(v, 0) + log1p(exp(-|v|)).  log1p(e) is evaluated as
-// log(w) * e / (w - 1) with w = 1 + e, the correction that makes log(1 + e)
-// accurate for small e (D. Goldberg, "What every computer scientist should know
-// about floating-point arithmetic", 1991, theorem 4); when w rounds to 1,
-// log1p(e) = e to working precision.
+// softplus(v) = max(v, 0) + log1p(e) with e = exp(-|v|) in (0, 1].  With
+// w = fl(1 + e), the rounding error d = (1 + e) - w = e - (w - 1) is computed
+// exactly (Dekker's Fast2Sum, "A floating-point technique for extending the
+// available precision", 1971: 1 >= e, and w - 1 is exact for w in [1, 2]), and
+// log1p(e) = log(w) + log(1 + d/w) = log(w) + d/w to first order.  d stands in
+// for d/w: they differ by d e / (1 + e), at most 2^-24 log1p(e).  When w
+// rounds to 1, log(w) = 0 and the result is e.
+__device__ __forceinline__ float log1p_of_exp_term(float e, float w) {
+  const float d = e - (w - 1.0f);
+  return __builtin_fmaf(__builtin_amdgcn_logf(w), kLn2, d);  // v_log_f32 is log2
+}
+
 __device__ __forceinline__ float softplus_f32(float v) {
   const float e = fast_exp2(-__builtin_fabsf(v) * kLog2e);
   const float w = 1.0f + e;
-  const float wm1 = w - 1.0f;
-  const float lg = __builtin_amdgcn_logf(w) * kLn2;  // v_log_f32 is log2
-  const float l1p = (wm1 == 0.0f) ? e : lg * (e * __builtin_amdgcn_rcpf(wm1));
-  return __builtin_fmaxf(v, 0.0f) + l1p;
+  return __builtin_fmaxf(v, 0.0f) + log1p_of_exp_term(e, w);
 }
 
 // DPP row_newbcast:S -- every lane of a 16-lane row reads lane S of that row.

@@ -134,12 +134,9 @@ __device__ __forceinline__ float sigmoid_f32(float v) { return __builtin_amdgcn_
 __device__ __forceinline__ float softplus_sigmoid_f32(float v, float& sig) {
   const float e = fast_exp2(-__builtin_fabsf(v) * kLog2e);
   const float w = 1.0f + e;
-  const float wm1 = w - 1.0f;
-  const float lg = __builtin_amdgcn_logf(w) * kLn2;
   const float rw = __builtin_amdgcn_rcpf(w);
   sig = (v >= 0.0f) ? rw : e * rw;
-  const float l1p = (wm1 == 0.0f) ? e : lg * (e * __builtin_amdgcn_rcpf(wm1));
-  return __builtin_fmaxf(v, 0.0f) + l1p;
+  return __builtin_fmaxf(v, 0.0f) + log1p_of_exp_term(e, w);
 }
 
 // Reduce-scatter over the 16 lanes of a DPP row: every lane holds v[0..15];
