@@ -555,6 +555,9 @@ __global__ __launch_bounds__(64 * W, 2) void ssm_bwd_kernel(BwdParams p) {
       Unroll<0, 16>::run([&]<int S>() {
         cy[0][S] = row_bcast<S>(c0) * y0;
         cy[1][S] = row_bcast<S>(c1) * y1;
+        // opaque from here: pass 2 reads the products, so the broadcasts are
+        // not kept to form them again there
+        asm volatile("" : "+v"(cy[0][S]), "+v"(cy[1][S]));
         mm[S] = ab[0][S] * __builtin_fmaf(ab[1][S], cy[1][S], cy[0][S]);
       });
     }
