@@ -191,7 +191,7 @@ __device__ __forceinline__ float row_reduce_scatter16(const float (&v)[16], int 
   // c ^ 2: keep q[0..1] (bit 1 clear) or q[2..3]
   const bool b1 = (c & 2) != 0, b0 = (c & 1) != 0;
   auto xchg = []<int CTRL>(float x) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xf, 0xf, true));
   };
   constexpr int kXor2 = 0x4e, kXor1 = 0xb1;  // quad_perm [2,3,0,1] and [1,0,3,2]
   const float r0 = (b1 ? q[2] : q[0]) + xchg.template operator()<kXor2>(b1 ? q[0] : q[2]);
