@@ -123,3 +123,25 @@ def test_delta_clamp_and_no_softplus():
     y, h = run_gpu(dev, delta_softplus=False)
     yr, hr = oracle_full(pos, delta_softplus=False)
     assert rel_err(to_np64(y), yr) <= 1e-4 and rel_err(to_np64(h), hr) <= 1e-4
+
+
+def test_softplus_over_its_whole_range():
+    """Raw delta from -40 to 40, so that softplus meets 1 + exp(-|v|) rounding
+    to 1 at both ends (the kernel's log1p then rests on the exact rounding
+    error of 1 + e alone) and every regime between; forward and backward
+    against the oracle at the fp32 bar."""
+    from test_gpu_bwd import _case, _compare, _gpu, _oracle
+    w = I.small_workload(I.WORKLOADS[0], batch=2, seqlen=300, dim=32)
+    inp = I.make_inputs(w, 4343)
+    rng = np.random.default_rng(4343)
+    raw = np.linspace(-40.0, 40.0, inp["delta"].size).astype(np.float32)
+    inp["delta"] = rng.permutation(raw).reshape(inp["delta"].shape)
+    dev = to_device(inp, "f32")
+    y, h = run_gpu(dev)
+    yr, hr = oracle_full(inp)
+    ey, eh = rel_err(to_np64(y), yr), rel_err(to_np64(h), hr)
+    print(f"forward: y {ey:.2e} h_last {eh:.2e}", flush=True)
+    assert ey <= tol_for("f32", "y") and eh <= tol_for("f32", "h_last")
+    _, binp = _case("f32", 16, 300, 2, 32, seed=4344)
+    binp["delta"] = rng.permutation(raw[: binp["delta"].size]).reshape(binp["delta"].shape)
+    _compare(_gpu(binp, "f32"), _oracle(binp), "f32", "backward")
